@@ -1,0 +1,275 @@
+// Host side of the C ABI declared in include/fvattn.h: argument validation,
+// workspace carving and kernel sequencing on the caller's stream.  No host
+// synchronisation and no device allocation happen here.
+#include <limits.h>
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "common.h"
+
+namespace fva {
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxBlocks = 2048;   // key blocks per row the routing sort holds
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned16(const void *p) { return p && ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void *p) { return p && ((uintptr_t)p & 3u) == 0; }
+
+fva_status make_geo(const fva_problem *p, Geo *g) {
+    if (!p) return FVA_ERR_INVALID_ARG;
+    if (p->batch < 0 || p->heads < 0) return FVA_ERR_INVALID_ARG;
+    if (p->grid_t < 1 || p->grid_y < 1 || p->grid_x < 1) return FVA_ERR_INVALID_ARG;
+    if (p->tile_t < 1 || p->tile_y < 1 || p->tile_x < 1) return FVA_ERR_INVALID_ARG;
+    if (p->dtype != FVA_BF16 && p->dtype != FVA_F32) return FVA_ERR_UNSUPPORTED;
+    if (p->head_dim != 64 && p->head_dim != 128) return FVA_ERR_UNSUPPORTED;
+    const int64_t vol = (int64_t)p->tile_t * p->tile_y * p->tile_x;
+    if (vol > kMaxSlots) return FVA_ERR_UNSUPPORTED;
+    const int64_t N = (int64_t)p->grid_t * p->grid_y * p->grid_x;
+    if (N >= INT32_MAX) return FVA_ERR_INVALID_ARG;
+    if (p->stride_n < p->head_dim || (p->stride_n % 8) || p->stride_h < 0 || (p->stride_h % 8) ||
+        p->stride_b < 0 || (p->stride_b % 8))
+        return FVA_ERR_INVALID_ARG;
+    const int64_t nT = (p->grid_t + p->tile_t - 1) / p->tile_t;
+    const int64_t nY = (p->grid_y + p->tile_y - 1) / p->tile_y;
+    const int64_t nX = (p->grid_x + p->tile_x - 1) / p->tile_x;
+    const int64_t Nb = nT * nY * nX;
+    if (Nb > kMaxBlocks) return FVA_ERR_UNSUPPORTED;
+    const int64_t BH = (int64_t)p->batch * p->heads;
+    if (BH * Nb * Nb >= INT32_MAX) return FVA_ERR_INVALID_ARG;
+    g->B = p->batch; g->H = p->heads; g->D = p->head_dim;
+    g->T = p->grid_t; g->Y = p->grid_y; g->X = p->grid_x;
+    g->tt = p->tile_t; g->ty = p->tile_y; g->tx = p->tile_x;
+    g->nT = (int)nT; g->nY = (int)nY; g->nX = (int)nX;
+    g->Nb = (int)Nb;
+    g->BH = (int)BH;
+    g->sb = p->stride_b; g->sh = p->stride_h; g->sn = p->stride_n;
+    g->dtype = p->dtype;
+    return FVA_OK;
+}
+
+// Per-device CU count cache (the library's only global state).
+std::mutex g_dev_mu;
+int g_dev_cus[64] = {0};
+
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (g_dev_cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        g_dev_cus[dev] = n;
+    }
+    return g_dev_cus[dev];
+}
+
+// ------------------------------------------------------ route workspace
+struct RouteWs {
+    size_t tok, bsize, qbar, kbar, sp, order, base, add, head_base, head_kept, total;
+};
+
+RouteWs route_layout(const Geo &g) {
+    RouteWs w;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+    const size_t R = (size_t)g.BH * g.Nb;
+    w.tok = take((size_t)g.Nb * kMaxSlots * 4);
+    w.bsize = take((size_t)g.Nb * 4);
+    w.qbar = take(R * g.D * 8);
+    w.kbar = take(R * g.D * 8);
+    w.sp = take(R * g.Nb * 8);
+    w.order = take(R * g.Nb * 4);
+    w.base = take(R * 4);
+    w.add = take(R * 4);
+    w.head_base = take((size_t)g.BH * 4);
+    w.head_kept = take((size_t)g.BH * 4);
+    w.total = off;
+    return w;
+}
+
+// -------------------------------------------------------- attn workspace
+struct AttnPlanSizes {
+    int num_ctas, cap_items, cap_parts, cap_splits;
+};
+
+fva_status attn_sizes(const Geo &g, const fva_attn_options *opts, AttnPlanSizes *s) {
+    int chunk = 0, ctas = 0;
+    if (opts) {
+        for (int i = 0; i < 6; ++i)
+            if (opts->reserved[i] != 0) return FVA_ERR_INVALID_ARG;
+        chunk = opts->chunk_blocks;
+        ctas = opts->num_ctas;
+        if (ctas < 0) return FVA_ERR_INVALID_ARG;
+    }
+    if (ctas == 0) {
+        const int cus = device_cus();
+        if (cus <= 0) return FVA_ERR_HIP;
+        ctas = cus * attention_ctas_per_cu(g);
+    }
+    const int64_t R = (int64_t)g.BH * g.Nb;
+    int64_t parts;
+    if (chunk < 0) parts = 0;
+    else if (chunk == 0) parts = 16LL * ctas;        // automatic chunks: <= 2 * total / C <= 16 * ctas
+    else parts = R * ((g.Nb + chunk - 1) / chunk);   // fixed chunks
+    if (parts > INT32_MAX / 2) return FVA_ERR_INVALID_ARG;
+    s->num_ctas = ctas;
+    s->cap_parts = (int)parts;
+    s->cap_splits = (int)(parts / 2);
+    s->cap_items = (int)(R + parts);
+    return FVA_OK;
+}
+
+struct AttnWs {
+    size_t tok, bsize, hdr, items, splits, part_o, part_ml, total;
+};
+
+AttnWs attn_layout(const Geo &g, const AttnPlanSizes &s) {
+    AttnWs w;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+    w.tok = take((size_t)g.Nb * kMaxSlots * 4);
+    w.bsize = take((size_t)g.Nb * 4);
+    w.hdr = take(sizeof(PlanHeader));
+    w.items = take((size_t)s.cap_items * sizeof(WorkItem));
+    w.splits = take((size_t)(s.cap_splits > 0 ? s.cap_splits : 1) * sizeof(SplitRow));
+    w.part_o = take((size_t)s.cap_parts * kMaxSlots * g.D * 4);
+    w.part_ml = take((size_t)s.cap_parts * kMaxSlots * 2 * 4);
+    w.total = off;
+    return w;
+}
+
+#define FVA_TRY_HIP(expr)                                  \
+    do {                                                   \
+        if ((expr) != hipSuccess) return FVA_ERR_HIP;      \
+    } while (0)
+
+}  // namespace
+}  // namespace fva
+
+using namespace fva;
+
+extern "C" {
+
+fva_status fva_num_blocks(const fva_problem *prob, int32_t *nq, int32_t *nk) {
+    Geo g;
+    const fva_status st = make_geo(prob, &g);
+    if (st != FVA_OK) return st;
+    if (!nq || !nk) return FVA_ERR_INVALID_ARG;
+    *nq = g.Nb;
+    *nk = g.Nb;
+    return FVA_OK;
+}
+
+size_t fva_lists_capacity(const fva_problem *prob) {
+    Geo g;
+    if (make_geo(prob, &g) != FVA_OK) return 0;
+    return (size_t)g.BH * g.Nb * g.Nb;
+}
+
+size_t fva_route_workspace_bytes(const fva_problem *prob) {
+    Geo g;
+    if (make_geo(prob, &g) != FVA_OK) return 0;
+    return route_layout(g).total;
+}
+
+fva_status fva_route(const fva_problem *prob, const void *q, const void *k, double p, int32_t kmin,
+                     fva_budget budget, const fva_lists *out, void *ws, size_t ws_bytes, void *stream) {
+    Geo g;
+    fva_status st = make_geo(prob, &g);
+    if (st != FVA_OK) return st;
+    if (!(p > 0.0 && p <= 1.0)) return FVA_ERR_INVALID_ARG;
+    if (kmin < 0) return FVA_ERR_INVALID_ARG;
+    if (budget.mode != FVA_BUDGET_NONE && budget.mode != FVA_BUDGET_FRAC && budget.mode != FVA_BUDGET_MATCH_MAX)
+        return FVA_ERR_INVALID_ARG;
+    if (budget.mode == FVA_BUDGET_FRAC && !(budget.frac >= 0.0 && budget.frac <= 1e6)) return FVA_ERR_INVALID_ARG;
+    if (!out || !aligned4(out->row_ptr) || !aligned4(out->col_idx)) return FVA_ERR_INVALID_ARG;
+    if (out->base_count && !aligned4(out->base_count)) return FVA_ERR_INVALID_ARG;
+    if (out->head_kept && !aligned4(out->head_kept)) return FVA_ERR_INVALID_ARG;
+    if (out->mask && !aligned4(out->mask)) return FVA_ERR_INVALID_ARG;
+    const bool empty = (g.BH == 0);
+    if (!empty && (!aligned16(q) || !aligned16(k))) return FVA_ERR_INVALID_ARG;
+    const RouteWs L = route_layout(g);
+    if (!ws || ws_bytes < L.total || ((uintptr_t)ws % kAlign)) return FVA_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    char *W = static_cast<char *>(ws);
+    int32_t *tok = (int32_t *)(W + L.tok), *bsize = (int32_t *)(W + L.bsize);
+    double *qbar = (double *)(W + L.qbar), *kbar = (double *)(W + L.kbar), *SP = (double *)(W + L.sp);
+    int32_t *order = (int32_t *)(W + L.order), *base = (int32_t *)(W + L.base), *add = (int32_t *)(W + L.add);
+    int32_t *head_base = (int32_t *)(W + L.head_base);
+    int32_t *head_kept = out->head_kept ? out->head_kept : (int32_t *)(W + L.head_kept);
+    if (!empty) {
+        FVA_TRY_HIP(launch_slot_table(g, tok, bsize, s));
+        FVA_TRY_HIP(launch_pool(g, q, tok, bsize, qbar, s));
+        FVA_TRY_HIP(launch_pool(g, k, tok, bsize, kbar, s));
+        FVA_TRY_HIP(launch_scores(g, qbar, kbar, SP, s));
+        FVA_TRY_HIP(launch_row_select(g, SP, order, base, p, kmin, s));
+        FVA_TRY_HIP(launch_augment(g, SP, base, add, head_base, head_kept, budget.mode, budget.frac, s));
+    }
+    FVA_TRY_HIP(launch_csr(g, order, base, add, out->row_ptr, out->col_idx, out->base_count, out->mask, s));
+    return FVA_OK;
+}
+
+size_t fva_attn_workspace_bytes(const fva_problem *prob, const fva_attn_options *opts) {
+    Geo g;
+    if (make_geo(prob, &g) != FVA_OK) return 0;
+    AttnPlanSizes sz;
+    if (attn_sizes(g, opts, &sz) != FVA_OK) return 0;
+    return attn_layout(g, sz).total;
+}
+
+size_t fva_attn_stats_bytes(const fva_problem *prob, const fva_attn_options *opts) {
+    Geo g;
+    if (make_geo(prob, &g) != FVA_OK) return 0;
+    AttnPlanSizes sz;
+    if (attn_sizes(g, opts, &sz) != FVA_OK) return 0;
+    return sizeof(fva_plan_info) + (size_t)sz.num_ctas * sizeof(fva_cta_stat);
+}
+
+fva_status fva_sparse_attn(const fva_problem *prob, const void *q, const void *k, const void *v,
+                           const fva_lists *lists, void *o, void *ws, size_t ws_bytes, void *stats,
+                           const fva_attn_options *opts, void *stream) {
+    Geo g;
+    fva_status st = make_geo(prob, &g);
+    if (st != FVA_OK) return st;
+    if (!lists || !aligned4(lists->row_ptr) || !aligned4(lists->col_idx)) return FVA_ERR_INVALID_ARG;
+    AttnPlanSizes sz;
+    st = attn_sizes(g, opts, &sz);
+    if (st != FVA_OK) return st;
+    if (g.BH == 0) return FVA_OK;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FVA_ERR_INVALID_ARG;
+    if (stats && ((uintptr_t)stats & 7u)) return FVA_ERR_INVALID_ARG;
+    const AttnWs L = attn_layout(g, sz);
+    if (!ws || ws_bytes < L.total || ((uintptr_t)ws % kAlign)) return FVA_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    char *W = static_cast<char *>(ws);
+    int32_t *tok = (int32_t *)(W + L.tok), *bsize = (int32_t *)(W + L.bsize);
+    PlanHeader *hdr = (PlanHeader *)(W + L.hdr);
+    WorkItem *items = (WorkItem *)(W + L.items);
+    SplitRow *splits = (SplitRow *)(W + L.splits);
+    float *part_o = (float *)(W + L.part_o), *part_ml = (float *)(W + L.part_ml);
+    const int chunk = opts ? opts->chunk_blocks : 0;
+    FVA_TRY_HIP(launch_slot_table(g, tok, bsize, s));
+    FVA_TRY_HIP(launch_plan(g, lists->row_ptr, chunk, sz.num_ctas, sz.cap_items, sz.cap_parts, hdr, items, splits, s));
+    FVA_TRY_HIP(launch_attention(g, q, k, v, o, lists->col_idx, tok, bsize, hdr, items, part_o, part_ml,
+                                 (fva_cta_stat *)stats, sz.num_ctas, s));
+    FVA_TRY_HIP(launch_combine(g, o, tok, bsize, hdr, splits, part_o, part_ml, sz.cap_splits, s));
+    return FVA_OK;
+}
+
+const char *fva_status_string(fva_status s) {
+    switch (s) {
+        case FVA_OK: return "FVA_OK";
+        case FVA_ERR_INVALID_ARG: return "FVA_ERR_INVALID_ARG: invalid argument";
+        case FVA_ERR_UNSUPPORTED: return "FVA_ERR_UNSUPPORTED: unsupported head_dim, dtype, tile volume or block count";
+        case FVA_ERR_WORKSPACE: return "FVA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+        case FVA_ERR_HIP: return "FVA_ERR_HIP: HIP runtime error";
+    }
+    return "unknown fva_status";
+}
+
+}  // extern "C"

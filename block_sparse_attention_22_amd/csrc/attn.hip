@@ -1,0 +1,604 @@
+// Block-sparse attention of FVAttn on gfx950: exact softmax attention over
+// the kept key blocks only (paperlayer.ai summary of FVAttn, section 2
+// "Background and Related Work": dynamic block-sparse attention; section 3
+// "FVAttn Design": Pipeline), plus the work-list balancer that is the one-GPU
+// counterpart of the pages' Runtime Load Balancing (section 3: attention
+// latency follows the largest workload, so long work is spread out).
+//
+//   plan_kernel      rows -> work items; rows longer than a chunk size are
+//                    split so that no item dominates a compute unit's share
+//   attn_bf16_kernel persistent workgroups pull items from a queue; per item
+//                    an online-softmax flash loop over the kept key blocks with
+//                    bf16 MFMA (v_mfma_f32_32x32x16_bf16) for Q K^T and P V
+//   attn_f32_kernel  the same contract in float32 arithmetic (small problems)
+//   combine_kernel   log-sum-exp merge of a split row's partial results
+//
+// MFMA data layout (32x32x16, wave64): the kernel computes S^T = K Q^T so that
+// each lane owns one query (column) and 16 keys per 32-key subtile.  The K
+// rows are fed to the MFMA in the order that makes a lane's 16 scores the
+// keys 16*(r/8) + 8*half + (r%8), i.e. two runs of 8 consecutive keys; those
+// 8 values, rounded to bf16, are exactly the B operand of O^T = V^T P^T for a
+// 16-key step.  Row max and row sum are therefore in-lane, plus one exchange
+// between the two half-waves.  V is stored transposed in LDS so its A operand
+// is one 16-byte read.  Both LDS tiles use an XOR swizzle of 16-byte chunks so
+// the MFMA operand reads and the tile writes are bank-conflict free.
+#include <float.h>
+#include <math.h>
+
+#include "common.h"
+
+namespace fva {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// Two floats -> two bf16 (round to nearest even) in one dword, low half first.
+__device__ inline uint32_t pack_bf16(float a, float b) {
+    const bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+struct AttnArgs {
+    Geo g;
+    const void *q, *k, *v;
+    void *o;
+    const int32_t *col_idx, *tok, *bsize;
+    PlanHeader *hdr;
+    const WorkItem *items;
+    float *part_o, *part_ml;
+    fva_cta_stat *stats;
+    float scale_log2;   // log2(e) / sqrt(D)
+};
+
+__device__ inline uint32_t hw_id_reg() {
+    uint32_t v;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(v));
+    return v;
+}
+__device__ inline uint32_t xcc_id_reg() {
+    uint32_t v;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+    return v;
+}
+
+__device__ inline void write_stats(const AttnArgs &a, uint64_t t0, uint32_t items, uint32_t blocks) {
+    if (!a.stats || threadIdx.x != 0) return;
+    const uint64_t t1 = wall_clock64();
+    fva_cta_stat st;
+    st.hw_id = hw_id_reg();
+    st.xcc_id = xcc_id_reg();
+    st.items = items;
+    st.blocks = blocks;
+    st.t_start = t0;
+    st.t_end = t1;
+    fva_cta_stat *rec = reinterpret_cast<fva_cta_stat *>(reinterpret_cast<char *>(a.stats) + sizeof(fva_plan_info));
+    rec[blockIdx.x] = st;
+    if (blockIdx.x == 0) *reinterpret_cast<fva_plan_info *>(a.stats) = a.hdr->info;
+}
+
+// Pull the next work item; every thread of the workgroup gets the same index.
+__device__ inline int next_item(PlanHeader *hdr, int *s_item) {
+    if (threadIdx.x == 0) *s_item = atomicAdd(&hdr->queue, 1);
+    __syncthreads();
+    const int it = *s_item;
+    __syncthreads();
+    return it;
+}
+
+// Swap bits 2 and 3 of a 5-bit MFMA row index: the K row fed to row x.
+__device__ inline int krow_of(int x) { return (x & 0x13) | ((x & 4) << 1) | ((x & 8) >> 1); }
+
+template <int D>
+struct TileRegs {
+    u32x4 k[D / 16];   // K: D/16 passes of 16 B per thread
+    u32x4 v[8];        // V: 8 slots x 16 B per thread (transposed on store)
+};
+
+// Global -> registers for key block j (128 slots; missing tokens read as 0).
+template <int D>
+__device__ __forceinline__ void load_tile(TileRegs<D> &tr, const int32_t *tj, const uint16_t *kb,
+                                          const uint16_t *vb, int64_t sn) {
+    constexpr int CH = D / 8, RP = 256 / CH, KP = kMaxSlots / RP;
+    const int tid = threadIdx.x;
+    const int c = tid % CH, r0 = tid / CH;
+#pragma unroll
+    for (int p = 0; p < KP; ++p) {
+        const int t = tj[r0 + p * RP];
+        tr.k[p] = (t >= 0) ? *reinterpret_cast<const u32x4 *>(kb + (int64_t)t * sn + c * 8) : u32x4{0, 0, 0, 0};
+    }
+    if (tid < CH * 16) {
+        const int cv = tid >> 4, g8 = tid & 15;
+        const int4 ta = *reinterpret_cast<const int4 *>(tj + 8 * g8);
+        const int4 tb = *reinterpret_cast<const int4 *>(tj + 8 * g8 + 4);
+        const int ts[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            tr.v[s] = (ts[s] >= 0) ? *reinterpret_cast<const u32x4 *>(vb + (int64_t)ts[s] * sn + cv * 8)
+                                   : u32x4{0, 0, 0, 0};
+    }
+}
+
+// Registers -> LDS.  K: row-major [slot][D], 16-byte chunk c of row s stored
+// at chunk c ^ (s % CH).  V: transposed [D][128 slots], 16-byte group g (8
+// slots) of row dd stored at group g ^ (dd % 16).
+template <int D>
+__device__ __forceinline__ void store_tile(const TileRegs<D> &tr, uint16_t *Kt, uint16_t *Vt) {
+    constexpr int CH = D / 8, RP = 256 / CH, KP = kMaxSlots / RP;
+    const int tid = threadIdx.x;
+    const int c = tid % CH, r0 = tid / CH;
+#pragma unroll
+    for (int p = 0; p < KP; ++p) {
+        const int slot = r0 + p * RP;
+        *reinterpret_cast<u32x4 *>(Kt + slot * D + ((c ^ (slot & (CH - 1))) << 3)) = tr.k[p];
+    }
+    if (tid < CH * 16) {
+        const int cv = tid >> 4, g8 = tid & 15;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int dd = 8 * cv + e;
+            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+            u32x4 out;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                out[w] = __builtin_amdgcn_perm(tr.v[2 * w + 1][e >> 1], tr.v[2 * w][e >> 1], sel);
+            *reinterpret_cast<u32x4 *>(Vt + dd * kMaxSlots + ((g8 ^ (dd & 15)) << 3)) = out;
+        }
+    }
+}
+
+// One key block for one wave's 32 queries.
+template <int D>
+__device__ __forceinline__ void compute_tile(const uint16_t *Kt, const uint16_t *Vt, int n_j, const bf16x8 *qf,
+                                             f32x16 *acc, float &m_run, float &l_run, float c, int h, int l32) {
+    constexpr int CH = D / 8, KS = D / 16, NU = D / 32;
+    const int nsub = (n_j + 31) >> 5;
+    const int krow = krow_of(l32);
+    f32x16 sacc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
+        if (t < nsub) {
+            const int slot = 32 * t + krow;
+            const uint16_t *kr = Kt + slot * D;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kr + (((2 * s + h) ^ (slot & (CH - 1))) << 3));
+                sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[t], 0, 0, 0);
+            }
+        }
+    }
+    if (n_j & 31) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (t == nsub - 1) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = 32 * t + 16 * (r >> 3) + 8 * h + (r & 7);
+                    if (key >= n_j) sacc[t][r] = -INFINITY;
+                }
+            }
+        }
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        if (t < nsub)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[t][r]);
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float mnew = fmaxf(m_run, mloc);
+    const float alpha = __builtin_amdgcn_exp2f((m_run - mnew) * c);
+    m_run = mnew;
+    const float mc = mnew * c;
+    l_run *= alpha;
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[u][r] *= alpha;
+    }
+    bf16x8 pf[8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        if (t < nsub) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[t][8 * hf + e], c, -mc));
+                    l_run += pv;
+                    pf[2 * t + hf][e] = (__bf16)pv;
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int sg = 0; sg < 8; ++sg) {
+        if (sg < 2 * nsub) {
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const int dd = 32 * u + l32;
+                const bf16x8 vf =
+                    *reinterpret_cast<const bf16x8 *>(Vt + dd * kMaxSlots + (((2 * sg + h) ^ (dd & 15)) << 3));
+                acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[sg], acc[u], 0, 0, 0);
+            }
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
+    constexpr int KS = D / 16, NU = D / 32;
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kMaxSlots * D];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][D * kMaxSlots];
+    __shared__ int s_item;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    const Geo &g = a.g;
+    const float c = a.scale_log2;
+    const uint64_t t0 = wall_clock64();
+    uint32_t n_done = 0, blocks_done = 0;
+    const int n_items = a.hdr->info.n_items;
+    const uint16_t *Q = static_cast<const uint16_t *>(a.q);
+    const uint16_t *K = static_cast<const uint16_t *>(a.k);
+    const uint16_t *V = static_cast<const uint16_t *>(a.v);
+    uint16_t *O = static_cast<uint16_t *>(a.o);
+
+    for (;;) {
+        const int it = next_item(a.hdr, &s_item);
+        if (it >= n_items) break;
+        const WorkItem wi = a.items[it];
+        const int bh = wi.row / g.Nb, i = wi.row - (wi.row / g.Nb) * g.Nb;
+        const int64_t boff = (int64_t)(bh / g.H) * g.sb + (int64_t)(bh % g.H) * g.sh;
+        const int n_i = a.bsize[i];
+        const bool active = (w * 32) < n_i;
+        const int qslot = w * 32 + l32;
+        const bool qvalid = qslot < n_i;
+        const int qtok = a.tok[i * kMaxSlots + qslot];
+        bf16x8 qf[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            u32x4 raw = qvalid ? *reinterpret_cast<const u32x4 *>(Q + boff + (int64_t)qtok * g.sn + 16 * s + 8 * h)
+                               : u32x4{0, 0, 0, 0};
+            qf[s] = __builtin_bit_cast(bf16x8, raw);
+        }
+        f32x16 acc[NU];
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[u][r] = 0.f;
+        float m_run = -INFINITY, l_run = 0.f;
+        const int nkb = wi.kb_end - wi.kb_begin;
+        if (nkb > 0) {
+            TileRegs<D> tr;
+            int j = a.col_idx[wi.kb_begin];
+            load_tile<D>(tr, a.tok + j * kMaxSlots, K + boff, V + boff, g.sn);
+            store_tile<D>(tr, Ks[0], Vs[0]);
+            __syncthreads();
+            for (int jj = 0; jj < nkb; ++jj) {
+                const int buf = jj & 1;
+                const int n_j = a.bsize[j];
+                int jn = j;
+                if (jj + 1 < nkb) {
+                    jn = a.col_idx[wi.kb_begin + jj + 1];
+                    load_tile<D>(tr, a.tok + jn * kMaxSlots, K + boff, V + boff, g.sn);
+                }
+                if (active) compute_tile<D>(Ks[buf], Vs[buf], n_j, qf, acc, m_run, l_run, c, h, l32);
+                if (jj + 1 < nkb) store_tile<D>(tr, Ks[buf ^ 1], Vs[buf ^ 1]);
+                __syncthreads();
+                j = jn;
+            }
+        }
+        const float l = l_run + __shfl_xor(l_run, 32, 64);
+        if (active && qvalid) {
+            if (wi.part < 0) {
+                const float inv = (l > 0.f) ? 1.f / l : 0.f;
+                uint16_t *orow = O + boff + (int64_t)qtok * g.sn;
+#pragma unroll
+                for (int u = 0; u < NU; ++u) {
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg) {
+                        const int dd = 32 * u + 8 * rg + 4 * h;
+                        uint32_t w01 = pack_bf16(acc[u][4 * rg] * inv, acc[u][4 * rg + 1] * inv);
+                        uint32_t w23 = pack_bf16(acc[u][4 * rg + 2] * inv, acc[u][4 * rg + 3] * inv);
+                        *reinterpret_cast<uint2 *>(orow + dd) = make_uint2(w01, w23);
+                    }
+                }
+            } else {
+                float *po = a.part_o + ((int64_t)wi.part * kMaxSlots + qslot) * D;
+#pragma unroll
+                for (int u = 0; u < NU; ++u)
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg) {
+                        const int dd = 32 * u + 8 * rg + 4 * h;
+                        *reinterpret_cast<float4 *>(po + dd) =
+                            make_float4(acc[u][4 * rg], acc[u][4 * rg + 1], acc[u][4 * rg + 2], acc[u][4 * rg + 3]);
+                    }
+                if (h == 0) {
+                    float *pm = a.part_ml + ((int64_t)wi.part * kMaxSlots + qslot) * 2;
+                    pm[0] = m_run * c;
+                    pm[1] = l;
+                }
+            }
+        }
+        ++n_done;
+        blocks_done += nkb;
+    }
+    write_stats(a, t0, n_done, blocks_done);
+}
+
+// Float32 path: one thread per query slot, K/V tiles of one key block in LDS.
+template <int D>
+__global__ __launch_bounds__(kMaxSlots, 1) void attn_f32_kernel(AttnArgs a) {
+    constexpr int D4 = D / 4;
+    __shared__ __attribute__((aligned(16))) float Ks[kMaxSlots * D];
+    __shared__ __attribute__((aligned(16))) float Vs[kMaxSlots * D];
+    __shared__ int s_item;
+    const int tid = threadIdx.x;
+    const Geo &g = a.g;
+    const float c = a.scale_log2;
+    const uint64_t t0 = wall_clock64();
+    uint32_t n_done = 0, blocks_done = 0;
+    const int n_items = a.hdr->info.n_items;
+    const float *Q = static_cast<const float *>(a.q);
+    const float *K = static_cast<const float *>(a.k);
+    const float *V = static_cast<const float *>(a.v);
+    float *O = static_cast<float *>(a.o);
+
+    for (;;) {
+        const int it = next_item(a.hdr, &s_item);
+        if (it >= n_items) break;
+        const WorkItem wi = a.items[it];
+        const int bh = wi.row / g.Nb, i = wi.row - (wi.row / g.Nb) * g.Nb;
+        const int64_t boff = (int64_t)(bh / g.H) * g.sb + (int64_t)(bh % g.H) * g.sh;
+        const int n_i = a.bsize[i];
+        const bool qvalid = tid < n_i;
+        const int qtok = a.tok[i * kMaxSlots + tid];
+        float qv[D], ov[D];
+#pragma unroll
+        for (int e = 0; e < D; ++e) {
+            qv[e] = qvalid ? Q[boff + (int64_t)qtok * g.sn + e] : 0.f;
+            ov[e] = 0.f;
+        }
+        float m = -INFINITY, l = 0.f;
+        const int nkb = wi.kb_end - wi.kb_begin;
+        for (int jj = 0; jj < nkb; ++jj) {
+            const int j = a.col_idx[wi.kb_begin + jj];
+            const int n_j = a.bsize[j];
+            __syncthreads();
+            for (int e = tid; e < n_j * D4; e += kMaxSlots) {
+                const int slot = e / D4, c4 = e - (e / D4) * D4;
+                const int t = a.tok[j * kMaxSlots + slot];
+                reinterpret_cast<float4 *>(Ks)[e] = reinterpret_cast<const float4 *>(K + boff + (int64_t)t * g.sn)[c4];
+                reinterpret_cast<float4 *>(Vs)[e] = reinterpret_cast<const float4 *>(V + boff + (int64_t)t * g.sn)[c4];
+            }
+            __syncthreads();
+            for (int key = 0; key < n_j; ++key) {
+                float s = 0.f;
+#pragma unroll
+                for (int e = 0; e < D; ++e) s = fmaf(qv[e], Ks[key * D + e], s);
+                s *= c;
+                if (s > m) {
+                    const float al = exp2f(m - s);
+                    l *= al;
+#pragma unroll
+                    for (int e = 0; e < D; ++e) ov[e] *= al;
+                    m = s;
+                }
+                const float p = exp2f(s - m);
+                l += p;
+#pragma unroll
+                for (int e = 0; e < D; ++e) ov[e] = fmaf(p, Vs[key * D + e], ov[e]);
+            }
+        }
+        if (qvalid) {
+            if (wi.part < 0) {
+                const float inv = (l > 0.f) ? 1.f / l : 0.f;
+                float *orow = O + boff + (int64_t)qtok * g.sn;
+#pragma unroll
+                for (int e = 0; e < D; e += 4)
+                    *reinterpret_cast<float4 *>(orow + e) = make_float4(ov[e] * inv, ov[e + 1] * inv, ov[e + 2] * inv, ov[e + 3] * inv);
+            } else {
+                float *po = a.part_o + ((int64_t)wi.part * kMaxSlots + tid) * D;
+#pragma unroll
+                for (int e = 0; e < D; e += 4) *reinterpret_cast<float4 *>(po + e) = make_float4(ov[e], ov[e + 1], ov[e + 2], ov[e + 3]);
+                float *pm = a.part_ml + ((int64_t)wi.part * kMaxSlots + tid) * 2;
+                pm[0] = m;
+                pm[1] = l;
+            }
+        }
+        ++n_done;
+        blocks_done += nkb;
+    }
+    write_stats(a, t0, n_done, blocks_done);
+}
+
+// ------------------------------------------------------------------ plan
+constexpr int kPlanThreads = 1024;
+
+template <typename T>
+__device__ inline T plan_scan(T x, T *tmp, T *total) {
+    const int t = threadIdx.x;
+    __syncthreads();
+    tmp[t] = x;
+    __syncthreads();
+    for (int off = 1; off < kPlanThreads; off <<= 1) {
+        T y = (t >= off) ? tmp[t - off] : T(0);
+        __syncthreads();
+        tmp[t] += y;
+        __syncthreads();
+    }
+    T incl = tmp[t];
+    *total = tmp[kPlanThreads - 1];
+    __syncthreads();
+    return incl - x;
+}
+
+__device__ inline int chunks_of(int cnt, int C) { return (cnt > C) ? (cnt + C - 1) / C : 1; }
+
+// Single workgroup.  Cost of a row = its kept key blocks.  chunk C: fixed,
+// none (INT_MAX) or automatic max(16, ceil(total / (8 * num_ctas))), which
+// keeps every item at most 1/8 of a workgroup's average share; a longer row
+// is cut into ceil(cnt / C) near-equal chunks, each a work item with its own
+// partial slot.  Items stay in (b, h, i) order so concurrently running
+// workgroups read the same head's keys and values.
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(int R, const int32_t *row_ptr, int chunk_mode,
+                                                            int num_ctas, int cap_items, int cap_parts,
+                                                            PlanHeader *hdr, WorkItem *items, SplitRow *splits) {
+    __shared__ int tmp[kPlanThreads];
+    const int tid = threadIdx.x;
+    const int seg = (R + kPlanThreads - 1) / kPlanThreads;
+    const int r0 = min(R, tid * seg), r1 = min(R, r0 + seg);
+    const int64_t total = row_ptr[R] - row_ptr[0];
+    int C;
+    if (chunk_mode < 0) C = INT32_MAX;
+    else if (chunk_mode > 0) C = chunk_mode;
+    else C = (int)max((int64_t)16, (total + 8LL * num_ctas - 1) / (8LL * num_ctas));
+
+    int n_items = 0, n_parts = 0, n_splits = 0;
+    int li, lp, ls;
+    for (int attempt = 0; attempt < 2; ++attempt) {
+        li = 0; lp = 0; ls = 0;
+        for (int r = r0; r < r1; ++r) {
+            const int n = chunks_of(row_ptr[r + 1] - row_ptr[r], C);
+            li += n;
+            if (n > 1) { lp += n; ls += 1; }
+        }
+        int ti, tp, ts;
+        plan_scan(li, tmp, &ti);
+        plan_scan(lp, tmp, &tp);
+        plan_scan(ls, tmp, &ts);
+        n_items = ti; n_parts = tp; n_splits = ts;
+        if (n_items <= cap_items && n_parts <= cap_parts) break;
+        C = INT32_MAX;     // cannot happen for the automatic size; never overrun the workspace
+    }
+    int item = 0, part = 0, spl = 0, dummy;
+    item = plan_scan(li, tmp, &dummy);
+    part = plan_scan(lp, tmp, &dummy);
+    spl = plan_scan(ls, tmp, &dummy);
+    for (int r = r0; r < r1; ++r) {
+        const int b0 = row_ptr[r], cnt = row_ptr[r + 1] - b0;
+        const int n = chunks_of(cnt, C);
+        if (n == 1) {
+            items[item++] = WorkItem{r, b0, b0 + cnt, -1};
+        } else {
+            splits[spl++] = SplitRow{r, part, n, 0};
+            for (int q = 0; q < n; ++q) {
+                const int s = b0 + (int)((int64_t)cnt * q / n);
+                const int e = b0 + (int)((int64_t)cnt * (q + 1) / n);
+                items[item++] = WorkItem{r, s, e, part++};
+            }
+        }
+    }
+    if (tid == 0) {
+        hdr->info.n_items = n_items;
+        hdr->info.chunk_blocks = C;
+        hdr->info.n_split_rows = n_splits;
+        hdr->info.n_partials = n_parts;
+        hdr->info.total_blocks = total;
+        hdr->info.num_ctas = num_ctas;
+        hdr->info.reserved = 0;
+        hdr->queue = 0;
+    }
+}
+
+// --------------------------------------------------------------- combine
+template <typename OutT>
+__device__ inline void store4(OutT *p, float4 v);
+template <>
+__device__ inline void store4<float>(float *p, float4 v) { *reinterpret_cast<float4 *>(p) = v; }
+template <>
+__device__ inline void store4<uint16_t>(uint16_t *p, float4 v) {
+    const uint32_t a = pack_bf16(v.x, v.y);
+    const uint32_t b = pack_bf16(v.z, v.w);
+    *reinterpret_cast<uint2 *>(p) = make_uint2(a, b);
+}
+
+template <typename OutT>
+__global__ __launch_bounds__(256) void combine_kernel(Geo g, OutT *O, const int32_t *tok, const int32_t *bsize,
+                                                      const PlanHeader *hdr, const SplitRow *splits,
+                                                      const float *part_o, const float *part_ml) {
+    const int n_split = hdr->info.n_split_rows;
+    const int D4 = g.D / 4;
+    for (int sidx = blockIdx.x; sidx < n_split; sidx += gridDim.x) {
+        const SplitRow sr = splits[sidx];
+        const int bh = sr.row / g.Nb, i = sr.row - (sr.row / g.Nb) * g.Nb;
+        const int64_t boff = (int64_t)(bh / g.H) * g.sb + (int64_t)(bh % g.H) * g.sh;
+        const int n_i = bsize[i];
+        for (int e = threadIdx.x; e < n_i * D4; e += 256) {
+            const int q = e / D4, c4 = e - (e / D4) * D4;
+            float M = -INFINITY;
+            for (int p = 0; p < sr.n_parts; ++p)
+                M = fmaxf(M, part_ml[((int64_t)(sr.part_begin + p) * kMaxSlots + q) * 2]);
+            float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+            float den = 0.f;
+            for (int p = 0; p < sr.n_parts; ++p) {
+                const int64_t pq = (int64_t)(sr.part_begin + p) * kMaxSlots + q;
+                const float mp = part_ml[pq * 2], lp = part_ml[pq * 2 + 1];
+                const float wgt = (mp == -INFINITY) ? 0.f : exp2f(mp - M);
+                const float4 ov = reinterpret_cast<const float4 *>(part_o + pq * g.D)[c4];
+                num.x += wgt * ov.x; num.y += wgt * ov.y; num.z += wgt * ov.z; num.w += wgt * ov.w;
+                den += wgt * lp;
+            }
+            const float inv = (den > 0.f) ? 1.f / den : 0.f;
+            const int t = tok[i * kMaxSlots + q];
+            store4<OutT>(O + boff + (int64_t)t * g.sn + 4 * c4,
+                         make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv));
+        }
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- launches
+int attention_ctas_per_cu(const Geo &) { return 1; }
+
+hipError_t launch_plan(const Geo &g, const int32_t *row_ptr, int chunk_mode, int num_ctas, int cap_items,
+                       int cap_parts, PlanHeader *hdr, WorkItem *items, SplitRow *splits, hipStream_t s) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, g.BH * g.Nb, row_ptr, chunk_mode, num_ctas,
+                       cap_items, cap_parts, hdr, items, splits);
+    return hipGetLastError();
+}
+
+hipError_t launch_attention(const Geo &g, const void *q, const void *k, const void *v, void *o,
+                            const int32_t *col_idx, const int32_t *tok, const int32_t *bsize, PlanHeader *hdr,
+                            const WorkItem *items, float *part_o, float *part_ml, fva_cta_stat *stats,
+                            int num_ctas, hipStream_t s) {
+    AttnArgs a;
+    a.g = g;
+    a.q = q; a.k = k; a.v = v; a.o = o;
+    a.col_idx = col_idx; a.tok = tok; a.bsize = bsize;
+    a.hdr = hdr; a.items = items;
+    a.part_o = part_o; a.part_ml = part_ml;
+    a.stats = stats;
+    a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.D));
+    if (g.dtype == FVA_BF16) {
+        if (g.D == 128) hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(num_ctas), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(num_ctas), dim3(256), 0, s, a);
+    } else {
+        if (g.D == 128) hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(num_ctas), dim3(kMaxSlots), 0, s, a);
+        else hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(num_ctas), dim3(kMaxSlots), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const Geo &g, void *o, const int32_t *tok, const int32_t *bsize, const PlanHeader *hdr,
+                          const SplitRow *splits, const float *part_o, const float *part_ml, int cap_splits,
+                          hipStream_t s) {
+    if (cap_splits <= 0) return hipSuccess;
+    const int grid = cap_splits < 1024 ? cap_splits : 1024;
+    if (g.dtype == FVA_BF16)
+        hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(grid), dim3(256), 0, s, g, (uint16_t *)o, tok, bsize, hdr,
+                           splits, part_o, part_ml);
+    else
+        hipLaunchKernelGGL(combine_kernel<float>, dim3(grid), dim3(256), 0, s, g, (float *)o, tok, bsize, hdr,
+                           splits, part_o, part_ml);
+    return hipGetLastError();
+}
+
+}  // namespace fva

@@ -1,0 +1,72 @@
+// Internal definitions shared by the HIP kernels and the host ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fvattn.h"
+
+namespace fva {
+
+constexpr int kMaxSlots = 128;   // tokens per block (tile volume) the kernels hold
+
+// Geometry derived from an fva_problem on the host and passed by value.
+struct Geo {
+    int B, H, D;
+    int T, Y, X;
+    int tt, ty, tx;
+    int nT, nY, nX;
+    int Nb;          // Nq = Nk
+    int BH;
+    int64_t sb, sh, sn;
+    int dtype;
+};
+
+// One unit of attention work: query-block row `row` (= (b*H + h)*Nb + i),
+// key-block range [kb_begin, kb_end) of col_idx, partial slot or -1.
+struct WorkItem {
+    int32_t row, kb_begin, kb_end, part;
+};
+
+// Split row bookkeeping for the combine step.
+struct SplitRow {
+    int32_t row, part_begin, n_parts, pad;
+};
+
+// Device-written plan header followed by the work queue counter.
+struct PlanHeader {
+    fva_plan_info info;
+    int32_t queue;
+    int32_t pad[7];
+};
+
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------- launches
+// Routing (route.hip)
+hipError_t launch_slot_table(const Geo &g, int32_t *tok, int32_t *bsize, hipStream_t s);
+hipError_t launch_pool(const Geo &g, const void *x, const int32_t *tok, const int32_t *bsize,
+                       double *out, hipStream_t s);
+hipError_t launch_scores(const Geo &g, const double *qbar, const double *kbar, double *S, hipStream_t s);
+hipError_t launch_row_select(const Geo &g, double *SP, int32_t *order, int32_t *base, double p,
+                             int kmin, hipStream_t s);
+hipError_t launch_augment(const Geo &g, const double *SP, const int32_t *base, int32_t *add,
+                          int32_t *head_base, int32_t *head_kept, int mode, double frac, hipStream_t s);
+hipError_t launch_csr(const Geo &g, const int32_t *order, const int32_t *base, const int32_t *add,
+                      int32_t *row_ptr, int32_t *col_idx, int32_t *base_out, uint32_t *mask,
+                      hipStream_t s);
+
+// Attention (attn.hip)
+hipError_t launch_plan(const Geo &g, const int32_t *row_ptr, int chunk_mode, int num_ctas,
+                       int cap_items, int cap_parts, PlanHeader *hdr, WorkItem *items,
+                       SplitRow *splits, hipStream_t s);
+hipError_t launch_attention(const Geo &g, const void *q, const void *k, const void *v, void *o,
+                            const int32_t *col_idx, const int32_t *tok, const int32_t *bsize,
+                            PlanHeader *hdr, const WorkItem *items, float *part_o, float *part_ml,
+                            fva_cta_stat *stats, int num_ctas, hipStream_t s);
+hipError_t launch_combine(const Geo &g, void *o, const int32_t *tok, const int32_t *bsize,
+                          const PlanHeader *hdr, const SplitRow *splits, const float *part_o,
+                          const float *part_ml, int cap_splits, hipStream_t s);
+int attention_ctas_per_cu(const Geo &g);
+
+}  // namespace fva

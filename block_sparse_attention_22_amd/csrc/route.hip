@@ -1,0 +1,521 @@
+// Sparse-routing front end of FVAttn on gfx950 (abstract: Top-p routing, a
+// Top-k safety floor and video-aware block organisation; paperlayer.ai
+// summary, section 3 "FVAttn Design": Sparse-routing frontend and
+// Slack-Aware Sparse Augmentation).
+//
+// Kernels, in launch order:
+//   slot_table   block -> its tokens in tile-local raster order (index math)
+//   pool         mean of Q / K over each block's tokens, float64
+//   scores       s_ij = qbar_i . kbar_j / sqrt(d), float64 tiled GEMM
+//   row_select   per query block: softmax, sort by (mass desc, index asc),
+//                prefix sums, Top-p cut, Top-k floor
+//   head_total / augment
+//                per head: budget, then the not-yet-kept blocks with the
+//                largest mass (ties to lower (i, j)) found by a radix search
+//                over the sorted row tails
+//   scan / csr   row_ptr and ascending col_idx from a per-row bitmask
+// All routing arithmetic is float64 so the lists are deterministic and match
+// an independent float64 evaluation except at cumulative masses within
+// rounding of p.
+#include <float.h>
+#include <math.h>
+
+#include "common.h"
+
+namespace fva {
+
+namespace {
+
+constexpr int kSortMax = 2048;   // key blocks a row may have
+
+__device__ inline double bits_to_double(uint64_t b) { return __longlong_as_double((long long)b); }
+__device__ inline uint64_t double_bits(double x) { return (uint64_t)__double_as_longlong(x); }
+
+template <typename T>
+__device__ inline T wave_sum(T x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+__device__ inline double wave_max(double x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmax(x, __shfl_xor(x, o, 64));
+    return x;
+}
+
+__device__ inline int wave_min(int x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o, 64));
+    return x;
+}
+
+// Block reductions for blockDim.x = NT (multiple of 64).  `red` holds NT/64
+// entries; the result is returned to every thread.
+template <int NT, typename T, typename Op>
+__device__ inline T block_reduce(T x, T *red, Op op) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = op(x, __shfl_xor(x, o, 64));
+    __syncthreads();
+    if (lane == 0) red[w] = x;
+    __syncthreads();
+    T r = red[0];
+#pragma unroll
+    for (int i = 1; i < NT / 64; ++i) r = op(r, red[i]);
+    return r;
+}
+
+// Exclusive block scan (sum) for blockDim.x = NT; `tmp` holds NT entries.
+template <int NT, typename T>
+__device__ inline T block_exclusive_scan(T x, T *tmp, T *total) {
+    const int t = threadIdx.x;
+    __syncthreads();
+    tmp[t] = x;
+    __syncthreads();
+    for (int off = 1; off < NT; off <<= 1) {
+        T y = (t >= off) ? tmp[t - off] : T(0);
+        __syncthreads();
+        tmp[t] += y;
+        __syncthreads();
+    }
+    T incl = tmp[t];
+    *total = tmp[NT - 1];
+    return incl - x;
+}
+
+// ------------------------------------------------------------ slot table
+// tok[b*128 + r] = token index of slot r of block b, or -1 past the block's
+// valid tokens; slots enumerate the tile's existing tokens in (t, y, x)
+// raster order so an edge tile's tokens are packed at the front.
+__global__ __launch_bounds__(kMaxSlots) void slot_table_kernel(Geo g, int32_t *tok, int32_t *bsize) {
+    const int b = blockIdx.x, r = threadIdx.x;
+    const int it = b / (g.nY * g.nX), iy = (b / g.nX) % g.nY, ix = b % g.nX;
+    const int et = min(g.tt, g.T - it * g.tt);
+    const int ey = min(g.ty, g.Y - iy * g.ty);
+    const int ex = min(g.tx, g.X - ix * g.tx);
+    const int n = et * ey * ex;
+    int t = -1;
+    if (r < n) {
+        const int dt = r / (ey * ex), rem = r % (ey * ex), dy = rem / ex, dx = rem % ex;
+        t = ((it * g.tt + dt) * g.Y + (iy * g.ty + dy)) * g.X + (ix * g.tx + dx);
+    }
+    tok[b * kMaxSlots + r] = t;
+    if (r == 0) bsize[b] = n;
+}
+
+// ------------------------------------------------------------------ pool
+__device__ inline void load8(const uint16_t *p, float *f) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ inline void load8(const float *p, float *f) {
+    const float4 a = reinterpret_cast<const float4 *>(p)[0];
+    const float4 b = reinterpret_cast<const float4 *>(p)[1];
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+// One workgroup per (block, batch*head); out[(bh*Nb + b)*D + c] = mean.
+template <typename T>
+__global__ __launch_bounds__(256) void pool_kernel(Geo g, const T *x, const int32_t *tok,
+                                                   const int32_t *bsize, double *out) {
+    __shared__ double red[256 * 8];
+    const int b = blockIdx.x, bh = blockIdx.y;
+    const int CH = g.D / 8, G = 256 / CH;
+    const int c = threadIdx.x % CH, grp = threadIdx.x / CH;
+    const T *base = x + (int64_t)(bh / g.H) * g.sb + (int64_t)(bh % g.H) * g.sh + c * 8;
+    const int n = bsize[b];
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int r = grp; r < n; r += G) {
+        const int t = tok[b * kMaxSlots + r];
+        float f[8];
+        load8(base + (int64_t)t * g.sn, f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += (double)f[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[grp * g.D + c * 8 + e] = acc[e];
+    __syncthreads();
+    for (int dd = threadIdx.x; dd < g.D; dd += 256) {
+        double s = 0.0;
+        for (int q = 0; q < G; ++q) s += red[q * g.D + dd];
+        out[((int64_t)bh * g.Nb + b) * g.D + dd] = s / (double)n;
+    }
+}
+
+// ---------------------------------------------------------------- scores
+// 64x64 output tile per workgroup; each thread 4x4 outputs (strided so the
+// LDS reads are conflict-free).  S[bh][i][j] = (qbar_i . kbar_j) / sqrt(D).
+__global__ __launch_bounds__(256) void scores_kernel(Geo g, const double *qbar, const double *kbar,
+                                                     double *S) {
+    __shared__ double qs[64][33];
+    __shared__ double ks[64][33];
+    const int j0 = blockIdx.x * 64, i0 = blockIdx.y * 64, bh = blockIdx.z;
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    const int Nb = g.Nb;
+    const double *qb = qbar + (int64_t)bh * Nb * g.D;
+    const double *kb = kbar + (int64_t)bh * Nb * g.D;
+    double acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+    for (int d0 = 0; d0 < g.D; d0 += 32) {
+        for (int e = threadIdx.x; e < 64 * 32; e += 256) {
+            const int r = e >> 5, cc = e & 31;
+            qs[r][cc] = (i0 + r < Nb) ? qb[(int64_t)(i0 + r) * g.D + d0 + cc] : 0.0;
+            ks[r][cc] = (j0 + r < Nb) ? kb[(int64_t)(j0 + r) * g.D + d0 + cc] : 0.0;
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int kk = 0; kk < 32; ++kk) {
+            double av[4], bv[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) av[a] = qs[ty + 16 * a][kk];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) bv[b] = ks[tx + 16 * b][kk];
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) acc[a][b] = fma(av[a], bv[b], acc[a][b]);
+        }
+        __syncthreads();
+    }
+    const double sq = sqrt((double)g.D);
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int i = i0 + ty + 16 * a;
+        if (i >= Nb) continue;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int j = j0 + tx + 16 * b;
+            if (j < Nb) S[((int64_t)bh * Nb + i) * Nb + j] = acc[a][b] / sq;
+        }
+    }
+}
+
+// ------------------------------------------------------------ row_select
+// One workgroup per (query block, batch*head).  Reads the score row, writes
+// the row's masses sorted descending (in place), the matching key-block
+// order, and the Top-p + floor count.
+__device__ inline bool before(double pa, int ia, double pb, int ib) {
+    return pa > pb || (pa == pb && ia < ib);
+}
+
+__global__ __launch_bounds__(256) void row_select_kernel(Geo g, double *SP, int32_t *order,
+                                                         int32_t *base, double p, int kmin, int NKP) {
+    __shared__ double val[kSortMax];
+    __shared__ int32_t idx[kSortMax];
+    __shared__ double dred[256];
+    __shared__ int ired[4];
+    const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+    const int Nk = g.Nb;
+    const int64_t rowoff = ((int64_t)bh * g.Nb + i) * Nk;
+
+    double mx = -INFINITY;
+    for (int j = tid; j < Nk; j += 256) {
+        const double s = SP[rowoff + j];
+        val[j] = s;
+        mx = fmax(mx, s);
+    }
+    mx = block_reduce<256>(mx, dred, [](double a, double b) { return fmax(a, b); });
+    double sum = 0.0;
+    for (int j = tid; j < Nk; j += 256) {
+        const double e = exp(val[j] - mx);
+        val[j] = e;
+        sum += e;
+    }
+    sum = block_reduce<256>(sum, dred, [](double a, double b) { return a + b; });
+    for (int j = tid; j < NKP; j += 256) {
+        val[j] = (j < Nk) ? val[j] / sum : -1.0;   // padding sorts last
+        idx[j] = j;
+    }
+    __syncthreads();
+
+    // Bitonic sort: final order is "before" (mass desc, index asc).
+    for (int kk = 2; kk <= NKP; kk <<= 1) {
+        for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+            for (int a = tid; a < NKP; a += 256) {
+                const int b = a ^ jj;
+                if (b > a) {
+                    const double va = val[a], vb = val[b];
+                    const int ia = idx[a], ib = idx[b];
+                    const bool up = (a & kk) == 0;
+                    const bool sw = up ? before(vb, ib, va, ia) : before(va, ia, vb, ib);
+                    if (sw) {
+                        val[a] = vb; val[b] = va;
+                        idx[a] = ib; idx[b] = ia;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // Inclusive prefix sums over contiguous per-thread segments.
+    const int seg = (Nk + 255) / 256;
+    const int s0 = min(Nk, tid * seg), s1 = min(Nk, s0 + seg);
+    double local = 0.0;
+    for (int j = s0; j < s1; ++j) local += val[j];
+    double total;
+    double run = block_exclusive_scan<256>(local, dred, &total);
+    int first = Nk;
+    for (int j = s0; j < s1; ++j) {
+        run += val[j];
+        if (run >= p) { first = j + 1; break; }
+    }
+    first = block_reduce<256>(first, ired, [](int a, int b) { return min(a, b); });
+    int m_p = (p >= 1.0) ? Nk : first;
+    const int m = min(Nk, max(m_p, kmin));
+
+    for (int j = tid; j < Nk; j += 256) {
+        SP[rowoff + j] = val[j];
+        order[rowoff + j] = idx[j];
+    }
+    if (tid == 0) base[(int64_t)bh * g.Nb + i] = m;
+}
+
+// --------------------------------------------------------------- augment
+__global__ __launch_bounds__(256) void head_total_kernel(Geo g, const int32_t *base, int32_t *head_base) {
+    __shared__ int red[4];
+    const int bh = blockIdx.x;
+    int s = 0;
+    for (int i = threadIdx.x; i < g.Nb; i += 256) s += base[(int64_t)bh * g.Nb + i];
+    s = block_reduce<256>(s, red, [](int a, int b) { return a + b; });
+    if (threadIdx.x == 0) head_base[bh] = s;
+}
+
+constexpr int kAugThreads = 1024;
+constexpr int kAugRows = 2;            // rows per thread: Nb <= 2048
+
+// First position in [lo, hi) of a descending sorted row whose bit pattern is
+// below t (every position before it holds a value >= t).
+__device__ inline int first_below(const double *row, int lo, int hi, uint64_t t) {
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (double_bits(row[mid]) >= t) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// One workgroup per (batch, head).  Chooses the A_h candidates (positions
+// r >= base_i of each row's sorted masses) with the largest mass, ties to
+// lower (i, j): a radix search over the IEEE bit pattern of the masses (four
+// bits per round, 15 thresholds at a time) finds the A_h-th largest mass
+// tau; rows take everything above tau, and the entries equal to tau go to
+// the lowest rows first (each row's equal entries are already in ascending j).
+__global__ __launch_bounds__(kAugThreads) void augment_kernel(Geo g, const double *SP, const int32_t *base,
+                                                              int32_t *add, const int32_t *head_base,
+                                                              int32_t *head_kept, int mode, double frac) {
+    __shared__ int cnt[16];
+    __shared__ int tmp[kAugThreads];
+    __shared__ int ired[kAugThreads / 64];
+    const int bh = blockIdx.x, tid = threadIdx.x;
+    const int b = bh / g.H;
+    const int Nb = g.Nb;
+    const int64_t NN = (int64_t)Nb * Nb;
+    const int K = head_base[bh];
+    int64_t Bh = K;
+    if (mode == FVA_BUDGET_FRAC) {
+        Bh = K + (int64_t)floor(frac * (double)K);
+        if (Bh > NN) Bh = NN;
+    } else if (mode == FVA_BUDGET_MATCH_MAX) {
+        for (int hh = 0; hh < g.H; ++hh) Bh = max(Bh, (int64_t)head_base[b * g.H + hh]);
+    }
+    const int A = (int)(Bh - K);
+    if (tid == 0) head_kept[bh] = (int)Bh;
+    const int32_t *hbase = base + (int64_t)bh * Nb;
+    int32_t *hadd = add + (int64_t)bh * Nb;
+    if (A <= 0) {
+        for (int i = tid; i < Nb; i += kAugThreads) hadd[i] = 0;
+        return;
+    }
+    // Contiguous rows per thread so the tie scan runs in row order.
+    const int seg = (Nb + kAugThreads - 1) / kAugThreads;
+    const int r0 = min(Nb, tid * seg);
+    const int nr = min(Nb, r0 + seg) - r0;
+    int lo[kAugRows], hi[kAugRows], m[kAugRows];
+#pragma unroll
+    for (int q = 0; q < kAugRows; ++q) {
+        m[q] = (q < nr) ? hbase[r0 + q] : 0;
+        lo[q] = m[q];
+        hi[q] = (q < nr) ? Nb : 0;
+    }
+    uint64_t x = 0;
+    for (int sh = 60; sh >= 0; sh -= 4) {
+        if (tid < 16) cnt[tid] = 0;
+        __syncthreads();
+        int pos[kAugRows][16];
+#pragma unroll
+        for (int q = 0; q < kAugRows; ++q) {
+            pos[q][0] = hi[q];
+            const double *row = SP + ((int64_t)bh * Nb + (q < nr ? r0 + q : 0)) * Nb;
+#pragma unroll
+            for (int v = 1; v < 16; ++v)
+                pos[q][v] = (q < nr) ? first_below(row, lo[q], hi[q], x | ((uint64_t)v << sh)) : 0;
+        }
+#pragma unroll
+        for (int v = 1; v < 16; ++v) {
+            int c = 0;
+#pragma unroll
+            for (int q = 0; q < kAugRows; ++q) c += (q < nr) ? pos[q][v] - m[q] : 0;
+            c = wave_sum(c);
+            if ((tid & 63) == 0) atomicAdd(&cnt[v], c);
+        }
+        __syncthreads();
+        int vs = 0;
+        for (int v = 15; v >= 1; --v)
+            if (cnt[v] >= A) { vs = v; break; }
+        x |= (uint64_t)vs << sh;
+#pragma unroll
+        for (int q = 0; q < kAugRows; ++q) {
+            int nlo = lo[q], nhi = hi[q];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                if (v == vs) nhi = pos[q][v];
+                if (v == vs + 1) nlo = pos[q][v];
+            }
+            hi[q] = nhi;
+            lo[q] = nlo;
+        }
+        __syncthreads();
+    }
+    // lo..hi now brackets the entries equal to tau; before lo: above tau.
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int q = 0; q < kAugRows; ++q)
+        if (q < nr) { gt += lo[q] - m[q]; eq += hi[q] - lo[q]; }
+    const int n_gt = block_reduce<kAugThreads>(gt, ired, [](int a, int c) { return a + c; });
+    int rem = A - n_gt;
+    int tot;
+    int pre = block_exclusive_scan<kAugThreads>(eq, tmp, &tot);
+#pragma unroll
+    for (int q = 0; q < kAugRows; ++q) {
+        if (q < nr) {
+            const int e = hi[q] - lo[q];
+            const int take = min(e, max(0, rem - pre));
+            pre += e;
+            hadd[r0 + q] = (lo[q] - m[q]) + take;
+        }
+    }
+}
+
+// ------------------------------------------------------------ scan / csr
+constexpr int kScanThreads = 1024;
+
+// row_ptr[r] = sum of (base + add) over rows before r; row_ptr[R] = total.
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(int R, const int32_t *base, const int32_t *add,
+                                                            int32_t *row_ptr, int32_t *base_out) {
+    __shared__ int tmp[kScanThreads];
+    const int tid = threadIdx.x;
+    const int seg = (R + kScanThreads - 1) / kScanThreads;
+    const int s0 = min(R, tid * seg), s1 = min(R, s0 + seg);
+    int local = 0;
+    for (int r = s0; r < s1; ++r) local += base[r] + add[r];
+    int total;
+    int run = block_exclusive_scan<kScanThreads>(local, tmp, &total);
+    for (int r = s0; r < s1; ++r) {
+        row_ptr[r] = run;
+        run += base[r] + add[r];
+        if (base_out) base_out[r] = base[r];
+    }
+    if (tid == 0) row_ptr[R] = total;
+}
+
+// One wave per row: bitmask of the first count entries of the row's order,
+// then set bits emitted in ascending order.
+__global__ __launch_bounds__(64) void csr_kernel(Geo g, const int32_t *order, const int32_t *row_ptr,
+                                                 int32_t *col_idx, uint32_t *mask) {
+    __shared__ uint32_t bits[64];
+    const int i = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
+    const int Nk = g.Nb;
+    const int64_t row = (int64_t)bh * g.Nb + i;
+    const int start = row_ptr[row], cnt = row_ptr[row + 1] - start;
+    const int W = (Nk + 31) / 32;
+    bits[lane] = 0;
+    __syncthreads();
+    const int32_t *ord = order + row * Nk;
+    for (int r = lane; r < cnt; r += 64) {
+        const int j = ord[r];
+        atomicOr(&bits[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+    const uint32_t word = (lane < W) ? bits[lane] : 0u;
+    const int pc = __popc(word);
+    int pre = pc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(pre, o, 64);
+        if (lane >= o) pre += y;
+    }
+    pre -= pc;
+    int pos = start + pre;
+    uint32_t wv = word;
+    while (wv) {
+        const int bit = __ffs(wv) - 1;
+        col_idx[pos++] = lane * 32 + bit;
+        wv &= wv - 1;
+    }
+    if (mask && lane < W) mask[row * W + lane] = word;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- launches
+hipError_t launch_slot_table(const Geo &g, int32_t *tok, int32_t *bsize, hipStream_t s) {
+    hipLaunchKernelGGL(slot_table_kernel, dim3(g.Nb), dim3(kMaxSlots), 0, s, g, tok, bsize);
+    return hipGetLastError();
+}
+
+hipError_t launch_pool(const Geo &g, const void *x, const int32_t *tok, const int32_t *bsize, double *out,
+                       hipStream_t s) {
+    const dim3 grid(g.Nb, g.BH);
+    if (g.dtype == FVA_BF16)
+        hipLaunchKernelGGL(pool_kernel<uint16_t>, grid, dim3(256), 0, s, g, (const uint16_t *)x, tok, bsize, out);
+    else
+        hipLaunchKernelGGL(pool_kernel<float>, grid, dim3(256), 0, s, g, (const float *)x, tok, bsize, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_scores(const Geo &g, const double *qbar, const double *kbar, double *S, hipStream_t s) {
+    const dim3 grid(ceil_div(g.Nb, 64), ceil_div(g.Nb, 64), g.BH);
+    hipLaunchKernelGGL(scores_kernel, grid, dim3(256), 0, s, g, qbar, kbar, S);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_select(const Geo &g, double *SP, int32_t *order, int32_t *base, double p, int kmin,
+                             hipStream_t s) {
+    int nkp = 256;
+    while (nkp < g.Nb) nkp <<= 1;
+    hipLaunchKernelGGL(row_select_kernel, dim3(g.Nb, g.BH), dim3(256), 0, s, g, SP, order, base, p, kmin, nkp);
+    return hipGetLastError();
+}
+
+hipError_t launch_augment(const Geo &g, const double *SP, const int32_t *base, int32_t *add, int32_t *head_base,
+                          int32_t *head_kept, int mode, double frac, hipStream_t s) {
+    hipLaunchKernelGGL(head_total_kernel, dim3(g.BH), dim3(256), 0, s, g, base, head_base);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(augment_kernel, dim3(g.BH), dim3(kAugThreads), 0, s, g, SP, base, add, head_base,
+                       head_kept, mode, frac);
+    return hipGetLastError();
+}
+
+hipError_t launch_csr(const Geo &g, const int32_t *order, const int32_t *base, const int32_t *add,
+                      int32_t *row_ptr, int32_t *col_idx, int32_t *base_out, uint32_t *mask, hipStream_t s) {
+    const int R = g.BH * g.Nb;
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, R, base, add, row_ptr, base_out);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || R == 0) return e;
+    hipLaunchKernelGGL(csr_kernel, dim3(g.Nb, g.BH), dim3(64), 0, s, g, order, row_ptr, col_idx, mask);
+    return hipGetLastError();
+}
+
+}  // namespace fva

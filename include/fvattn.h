@@ -1,0 +1,194 @@
+/*
+ * fvattn.h - C ABI of the FVAttn block-sparse attention hot path for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The library implements the single-GPU data-parallel path of FVAttn
+ * ("FVAttn: Adaptive Sparse Attention with Runtime Load Balancing for Video
+ * Generation", arXiv 2607.16190):
+ *
+ *   fva_route        the sparse-routing front end: video-aware 3D-tile blocks,
+ *                    mean-pooled Q/K block scores, per-query-block Top-p cut
+ *                    with a Top-k floor, slack-aware augmentation up to a
+ *                    per-head budget, and the per-head CSR block lists
+ *                    (abstract; paperlayer.ai summary, section 3 "FVAttn
+ *                    Design": Sparse-routing frontend, Slack-Aware Sparse
+ *                    Augmentation);
+ *   fva_sparse_attn  exact softmax attention over only the kept key blocks
+ *                    (section 2 "Background and Related Work": dynamic
+ *                    block-sparse attention), with a work-list balancer that
+ *                    spreads long rows over the GPU's compute units - the
+ *                    one-GPU counterpart of the pages' Runtime Load Balancing
+ *                    (section 3, "Runtime Load Balancing").
+ *
+ * Conventions shared by every entry point:
+ *  - Ownership: the caller owns every buffer (inputs, outputs, workspace,
+ *    stats).  The library allocates no device memory and keeps no per-call
+ *    state; its only global state is a per-device cache of the CU count.
+ *  - Asynchrony: device work is enqueued on `stream` (a hipStream_t; NULL is
+ *    the null stream) and the host is never synchronised.  Every
+ *    data-dependent size stays on the device; outputs are sized for the
+ *    worst case.  Concurrent calls on one stream are ordered; calls that
+ *    share a workspace on different streams race.
+ *  - Validation: arguments are checked on the host before anything is
+ *    launched; on error nothing is enqueued and outputs are untouched.  A
+ *    launch failure returns FVA_ERR_HIP (outputs then undefined).  No
+ *    exception crosses the ABI.  Calls are thread-safe.
+ *  - Pointers marked "device" must be device (or managed) memory, 16-byte
+ *    aligned.
+ */
+#ifndef FVATTN_H
+#define FVATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FVA_OK = 0,
+    FVA_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, bad size or parameter */
+    FVA_ERR_UNSUPPORTED = -2,   /* valid but not implemented (head_dim, dtype, tile volume) */
+    FVA_ERR_WORKSPACE = -3,     /* workspace smaller than the matching *_workspace_bytes */
+    FVA_ERR_HIP = -4            /* a HIP runtime call or launch failed */
+} fva_status;
+
+typedef enum { FVA_BF16 = 0, FVA_F32 = 1 } fva_dtype;
+
+/*
+ * Problem geometry.  Q, K, V and O are [batch, heads, N, head_dim] with
+ * N = grid_t*grid_y*grid_x latent tokens, token n = (t*grid_y + y)*grid_x + x,
+ * head_dim contiguous, and the given element strides (identical for q, k, v
+ * and o; stride_n >= head_dim, all multiples of 8).
+ *
+ * Blocks are 3D tiles of tile_t x tile_y x tile_x tokens in raster order over
+ * the tile grid: block b = (it*nY + iy)*nX + ix with nT = ceil(grid_t/tile_t),
+ * nY = ceil(grid_y/tile_y), nX = ceil(grid_x/tile_x) (the pages' "video-aware
+ * block organisation").  A tile on the far edge of an axis that is not a
+ * multiple of the tile size holds only the tokens that exist; missing tokens
+ * are never keys and produce no output.  Nq = Nk = nT*nY*nX.
+ *
+ * Supported: head_dim in {64, 128}; dtype FVA_BF16 or FVA_F32;
+ * tile volume tile_t*tile_y*tile_x <= 128; batch*heads*Nq*Nk < 2^31.
+ * batch == 0 or heads == 0 is a valid empty problem (every call is a no-op).
+ */
+typedef struct {
+    int32_t batch, heads, head_dim;
+    int32_t grid_t, grid_y, grid_x;
+    int32_t tile_t, tile_y, tile_x;
+    int32_t dtype;                 /* fva_dtype */
+    int64_t stride_b, stride_h, stride_n;
+} fva_problem;
+
+/*
+ * Slack budget of the augmentation step, per (batch, head), where K_h is the
+ * head's block count after Top-p and the floor:
+ *   NONE      B_h = K_h (no augmentation);
+ *   FRAC      B_h = min(Nq*Nk, K_h + floor(frac*K_h)), frac >= 0, computed in
+ *             IEEE double;
+ *   MATCH_MAX B_h = max over heads h' of the same batch item of K_h'.
+ */
+typedef enum { FVA_BUDGET_NONE = 0, FVA_BUDGET_FRAC = 1, FVA_BUDGET_MATCH_MAX = 2 } fva_budget_mode;
+typedef struct {
+    int32_t mode;                  /* fva_budget_mode */
+    double frac;
+} fva_budget;
+
+/*
+ * Block lists: one CSR row per (batch, head, query block), rows in
+ * (b, h, i) order, each row's kept key blocks in ascending order.
+ * All device int32 buffers owned by the caller.
+ */
+typedef struct {
+    int32_t *row_ptr;     /* [batch*heads*Nq + 1], required */
+    int32_t *col_idx;     /* [fva_lists_capacity()], required; entries past row_ptr[last] undefined */
+    int32_t *base_count;  /* [batch*heads*Nq] kept blocks before augmentation; may be NULL */
+    int32_t *head_kept;   /* [batch*heads] final kept blocks per head (= B_h); may be NULL */
+    uint32_t *mask;       /* [batch*heads*Nq*ceil(Nk/32)] bit j of row r = block j kept; may be NULL */
+} fva_lists;
+
+/* Balancer options for fva_sparse_attn; pass NULL for the defaults (all 0). */
+typedef struct {
+    /* Split rows into work items of at most this many key blocks:
+     *  0  automatic: C = max(16, ceil(total kept blocks / (8 * num_ctas)));
+     *  <0 never split (one work item per row);
+     *  >0 this chunk size. */
+    int32_t chunk_blocks;
+    /* Persistent workgroups; 0 = one per compute unit of the current device. */
+    int32_t num_ctas;
+    int32_t reserved[6];  /* must be 0 */
+} fva_attn_options;
+
+/* Written by the device into the optional stats buffer of fva_sparse_attn. */
+typedef struct {
+    int32_t n_items;       /* work items executed */
+    int32_t chunk_blocks;  /* chunk size the plan used (INT32_MAX = no split) */
+    int32_t n_split_rows;  /* rows split into more than one item */
+    int32_t n_partials;    /* partial results merged by the combine step */
+    int64_t total_blocks;  /* kept (query block, key block) pairs */
+    int32_t num_ctas;      /* persistent workgroups launched */
+    int32_t reserved;
+} fva_plan_info;
+
+typedef struct {
+    uint32_t hw_id;        /* raw HW_ID register of the workgroup's first wave */
+    uint32_t xcc_id;       /* raw XCC_ID register (accelerator complex die) */
+    uint32_t items;        /* work items this workgroup processed */
+    uint32_t blocks;       /* key blocks this workgroup processed */
+    uint64_t t_start;      /* constant-rate (100 MHz) device clock at start */
+    uint64_t t_end;        /* ... and after its last item */
+} fva_cta_stat;
+
+/* Number of query and key blocks of a problem.  Host only; FVA_ERR_* on an
+ * invalid or unsupported problem. */
+fva_status fva_num_blocks(const fva_problem *prob, int32_t *nq, int32_t *nk);
+
+/* col_idx capacity in entries: batch*heads*Nq*Nk (0 if the problem is invalid). */
+size_t fva_lists_capacity(const fva_problem *prob);
+
+/* Workspace bytes fva_route needs (0 if the problem is invalid). */
+size_t fva_route_workspace_bytes(const fva_problem *prob);
+
+/*
+ * Routing front end.  q, k: device, layout of `prob`.  p in (0, 1]: Top-p
+ * mass (p = 1 keeps every block); kmin >= 0: Top-k floor (clamped to Nk).
+ * Scores, softmax and cumulative masses are computed in float64; key blocks
+ * are ranked by mass descending with ties to the lower block index.
+ * Writes `out`'s buffers; ws: device workspace of at least
+ * fva_route_workspace_bytes(prob) bytes.
+ */
+fva_status fva_route(const fva_problem *prob, const void *q, const void *k, double p, int32_t kmin,
+                     fva_budget budget, const fva_lists *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes fva_sparse_attn needs for these options (NULL = defaults).
+ * With num_ctas == 0 this queries the current device (0 if that fails). */
+size_t fva_attn_workspace_bytes(const fva_problem *prob, const fva_attn_options *opts);
+
+/* Bytes of the stats buffer: one fva_plan_info then one fva_cta_stat per
+ * persistent workgroup (0 if the problem or options are invalid). */
+size_t fva_attn_stats_bytes(const fva_problem *prob, const fva_attn_options *opts);
+
+/*
+ * Block-sparse attention: for every query token t of block i,
+ *   o_t = sum_u softmax_u(q_t . k_u / sqrt(head_dim)) v_u
+ * over the tokens u of row i's kept key blocks (lists->row_ptr/col_idx as
+ * written by fva_route, or any CSR with ascending or unordered, in-range,
+ * duplicate-free columns).  q, k, v, o: device, layout of `prob`, o in the
+ * input dtype.  bf16 inputs use bf16 MFMA with float32 accumulation and an
+ * online softmax; float32 inputs use float32 arithmetic throughout.  A row
+ * with no kept block yields zeros.  stats: NULL or a device buffer of
+ * fva_attn_stats_bytes(prob, opts) bytes.  Only row_ptr and col_idx of
+ * `lists` are read.
+ */
+fva_status fva_sparse_attn(const fva_problem *prob, const void *q, const void *k, const void *v,
+                           const fva_lists *lists, void *o, void *ws, size_t ws_bytes, void *stats,
+                           const fva_attn_options *opts, void *stream);
+
+/* Static string naming a status code. */
+const char *fva_status_string(fva_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FVATTN_H */

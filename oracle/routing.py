@@ -146,8 +146,15 @@ def route_head(q: np.ndarray, k: np.ndarray, layout: BlockLayout, p: float, kmin
     return dict(qbar=qbar, kbar=kbar, s=s, P=P, order=order, base=m, cum=c)
 
 
-def route(q, k, layout: BlockLayout, p: float, kmin: int, budget=("none", 0.0)) -> Dict:
+def _route_head_args(args):
+    return route_head(*args)
+
+
+def route(q, k, layout: BlockLayout, p: float, kmin: int, budget=("none", 0.0), map_fn=map) -> Dict:
     """Full front end (O2-O7) over q, k [B, H, N, d].
+
+    ``map_fn`` evaluates the independent per-head steps O2-O5 (e.g. a process
+    pool's ``map``); augmentation and CSR then run in (b, h) order.
 
     Returns a dict with per-head lists (``heads[b][h]``) and the flattened
     (b, h, i)-ordered arrays ``base`` [B*H*Nq], ``count`` [B*H*Nq],
@@ -158,7 +165,8 @@ def route(q, k, layout: BlockLayout, p: float, kmin: int, budget=("none", 0.0)) 
     B, H = q.shape[:2]
     Nq = Nk = layout.Nb
     mode, frac = budget
-    heads = [[route_head(q[b, h], k[b, h], layout, p, kmin) for h in range(H)] for b in range(B)]
+    flat = list(map_fn(_route_head_args, [(q[b, h], k[b, h], layout, p, kmin) for b in range(B) for h in range(H)]))
+    heads = [flat[b * H:(b + 1) * H] for b in range(B)]
     base, count, cols, kept = [], [], [], []
     for b in range(B):
         K = np.array([heads[b][h]["base"].sum() for h in range(H)], dtype=np.int64)

@@ -1,0 +1,172 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function the
+header declares, answers host-only queries, and rejects bad arguments before
+launching anything (no GPU is touched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_22_amd as fva
+from block_sparse_attention_22_amd import (AttnOptions, Budget, ListsC, Problem, FVA_OK, FVA_ERR_INVALID_ARG,
+                                           FVA_ERR_UNSUPPORTED, FVA_ERR_WORKSPACE)
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fvattn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fva.LIB_PATH):          # fresh checkout: build once (hipcc cross-compiles)
+        from block_sparse_attention_22_amd import build as _b
+        _b.build()
+    return fva.load_library()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fva_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert set(header_functions()) == set(fva.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def prob(**kw):
+    base = dict(batch=1, heads=40, head_dim=128, grid_t=21, grid_y=45, grid_x=80, tile_t=2, tile_y=8, tile_x=8,
+                dtype=0, stride_b=40 * 75600 * 128, stride_h=75600 * 128, stride_n=128)
+    base.update(kw)
+    return Problem(**base)
+
+
+def nblocks(lib, p):
+    nq, nk = ctypes.c_int32(), ctypes.c_int32()
+    st = lib.fva_num_blocks(ctypes.byref(p), ctypes.byref(nq), ctypes.byref(nk))
+    return st, nq.value, nk.value
+
+
+@pytest.mark.parametrize("grid,tile,nb", [((21, 45, 80), (2, 8, 8), 660), ((21, 68, 120), (2, 8, 8), 1485),
+                                          ((5, 30, 52), (2, 8, 8), 84), ((4, 8, 8), (1, 8, 8), 4),
+                                          ((1, 5, 5), (2, 8, 8), 1)])
+def test_num_blocks(lib, grid, tile, nb):
+    p = prob(grid_t=grid[0], grid_y=grid[1], grid_x=grid[2], tile_t=tile[0], tile_y=tile[1], tile_x=tile[2])
+    assert nblocks(lib, p) == (FVA_OK, nb, nb)
+    assert lib.fva_lists_capacity(ctypes.byref(p)) == 40 * nb * nb
+
+
+def test_route_workspace_is_host_only_and_sized(lib):
+    p = prob()
+    ws = lib.fva_route_workspace_bytes(ctypes.byref(p))
+    R = 40 * 660
+    assert ws >= R * 660 * (8 + 4) + 2 * R * 128 * 8
+
+
+def test_attn_workspace_with_explicit_ctas(lib):
+    p = prob()
+    o = AttnOptions()
+    o.num_ctas = 256
+    ws_auto = lib.fva_attn_workspace_bytes(ctypes.byref(p), ctypes.byref(o))
+    assert ws_auto >= 16 * 256 * 128 * 128 * 4            # partial slots of the automatic split
+    o.chunk_blocks = -1
+    assert lib.fva_attn_workspace_bytes(ctypes.byref(p), ctypes.byref(o)) < ws_auto
+    assert lib.fva_attn_stats_bytes(ctypes.byref(p), ctypes.byref(o)) == \
+        ctypes.sizeof(fva.PlanInfo) + 256 * ctypes.sizeof(fva.CtaStat)
+    o.reserved[2] = 1
+    assert lib.fva_attn_workspace_bytes(ctypes.byref(p), ctypes.byref(o)) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), FVA_ERR_UNSUPPORTED), (dict(dtype=7), FVA_ERR_UNSUPPORTED),
+    (dict(tile_t=4, tile_y=8, tile_x=8), FVA_ERR_UNSUPPORTED),          # 256-token tile
+    (dict(grid_t=0), FVA_ERR_INVALID_ARG), (dict(tile_x=0), FVA_ERR_INVALID_ARG),
+    (dict(batch=-1), FVA_ERR_INVALID_ARG), (dict(stride_n=100), FVA_ERR_INVALID_ARG),
+    (dict(stride_n=132), FVA_ERR_INVALID_ARG),
+    (dict(grid_t=64, grid_y=64, grid_x=64, tile_t=1, tile_y=8, tile_x=8), FVA_ERR_UNSUPPORTED),  # 4096 blocks
+])
+def test_bad_problems_rejected(lib, kw, code):
+    p = prob(**kw)
+    assert nblocks(lib, p)[0] == code
+    assert lib.fva_lists_capacity(ctypes.byref(p)) == 0
+    assert lib.fva_route_workspace_bytes(ctypes.byref(p)) == 0
+
+
+def test_overflowing_list_count_rejected(lib):
+    p = prob(heads=1300, grid_t=22, grid_y=64, grid_x=120)     # 1300 heads x 1320^2 blocks > 2^31
+    assert nblocks(lib, p)[0] == FVA_ERR_INVALID_ARG
+
+
+def test_null_problem(lib):
+    assert lib.fva_num_blocks(None, ctypes.byref(ctypes.c_int32()), ctypes.byref(ctypes.c_int32())) == \
+        FVA_ERR_INVALID_ARG
+
+
+# Fake 256-byte-aligned addresses: validation must reject before any use.
+Q = 1 << 20
+GOOD_LISTS = ListsC(Q, Q, None, None, None)
+
+
+def route_call(lib, p=None, q=Q, k=Q, pv=0.9, kmin=4, budget=Budget(1, 0.1), lists=GOOD_LISTS, ws=Q, wsb=0):
+    p = p or prob()
+    return lib.fva_route(ctypes.byref(p), q, k, pv, kmin, budget, ctypes.byref(lists) if lists else None, ws, wsb,
+                         None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(pv=0.0), FVA_ERR_INVALID_ARG), (dict(pv=1.5), FVA_ERR_INVALID_ARG),
+    (dict(pv=float("nan")), FVA_ERR_INVALID_ARG), (dict(kmin=-1), FVA_ERR_INVALID_ARG),
+    (dict(budget=Budget(5, 0.0)), FVA_ERR_INVALID_ARG), (dict(budget=Budget(1, -0.5)), FVA_ERR_INVALID_ARG),
+    (dict(lists=None), FVA_ERR_INVALID_ARG), (dict(lists=ListsC(None, Q, None, None, None)), FVA_ERR_INVALID_ARG),
+    (dict(q=None), FVA_ERR_INVALID_ARG), (dict(k=Q + 8), FVA_ERR_INVALID_ARG),
+    (dict(ws=None), FVA_ERR_WORKSPACE), (dict(wsb=1024), FVA_ERR_WORKSPACE),
+    (dict(p=prob(head_dim=32)), FVA_ERR_UNSUPPORTED),
+])
+def test_route_rejects_before_launch(lib, kw, code):
+    assert route_call(lib, **kw) == code
+
+
+def attn_call(lib, p=None, q=Q, k=Q, v=Q, o=Q, lists=GOOD_LISTS, ws=Q, wsb=0, stats=None, opts=None):
+    p = p or prob()
+    if opts is None:
+        opts = AttnOptions()
+        opts.num_ctas = 256
+    return lib.fva_sparse_attn(ctypes.byref(p), q, k, v, ctypes.byref(lists) if lists else None, o, ws, wsb, stats,
+                               ctypes.byref(opts), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lists=None), FVA_ERR_INVALID_ARG), (dict(v=None), FVA_ERR_INVALID_ARG), (dict(o=Q + 4), FVA_ERR_INVALID_ARG),
+    (dict(ws=None), FVA_ERR_WORKSPACE), (dict(wsb=4096), FVA_ERR_WORKSPACE), (dict(stats=Q + 3), FVA_ERR_INVALID_ARG),
+    (dict(p=prob(dtype=3)), FVA_ERR_UNSUPPORTED),
+])
+def test_attn_rejects_before_launch(lib, kw, code):
+    assert attn_call(lib, **kw) == code
+
+
+def test_attn_rejects_bad_options(lib):
+    o = AttnOptions()
+    o.num_ctas = -3
+    assert attn_call(lib, opts=o) == FVA_ERR_INVALID_ARG
+    o = AttnOptions()
+    o.num_ctas = 8
+    o.reserved[0] = 9
+    assert attn_call(lib, opts=o) == FVA_ERR_INVALID_ARG
+
+
+def test_empty_problem_attention_is_noop(lib):
+    o = AttnOptions()
+    o.num_ctas = 4
+    assert attn_call(lib, p=prob(heads=0), q=None, k=None, v=None, o=None, ws=None, opts=o) == FVA_OK
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, -4):
+        assert lib.fva_status_string(s).startswith(b"FVA_")
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError):
+        fva.load_library(str(tmp_path / "missing.so"))

@@ -1,0 +1,201 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every workload runs at its full size in the launch configuration the bench
+times (default balancer options).  Block lists are compared in full; outputs
+on every row for the small workloads and on a seeded sample of query blocks
+per head for the 75,600- and 171,360-token layers.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_22_amd as fva
+from oracle import BlockLayout, attention, routing
+from workloads import WORKLOADS, make_inputs, sample_qblocks, tiny_random
+
+from parity import attention_error, compare_lists, gpu_lists_to_host, to_numpy
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+SAMPLE = {1: None, 2: None, 3: 16, 4: 16, 5: 64}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return torch.device("cuda:0")
+
+
+def _rows_sample(w, nb, n):
+    if n is None:
+        return None
+    rng = np.random.default_rng((260716190, w.cid, 1))
+    return {bh: np.sort(rng.choice(nb, min(n, nb), replace=False)) for bh in range(w.B * w.H)}
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_workload_parity(dev, cid):
+    w = WORKLOADS[cid]
+    print(f"\n[parity] config {cid} {w.name}: generating", flush=True)
+    q, k, v, _ = make_inputs(w)
+    lay = BlockLayout(w.grid, w.tile)
+    npdt = np.float64 if cid <= 2 else np.float32
+    qn, kn, vn = (to_numpy(t, npdt) for t in (q, k, v))
+    ref = routing.route(qn, kn, lay, w.p, w.kmin, w.budget)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    print(f"[parity] config {cid}: route on GPU", flush=True)
+    lists = fva.route(qd, kd, w.p, w.kmin, w.budget, grid=w.grid, tile=w.tile)
+    g = gpu_lists_to_host(lists)
+    rep = compare_lists(g, ref, w.p, w.budget, lay, w.B, w.H)
+    print(f"[parity] config {cid}: lists {rep}", flush=True)
+    assert rep["exact_rows"] + rep["excused_count_rows"] + rep["excused_tie_rows"] >= rep["rows"]
+    # determinism of the routing
+    lists2 = fva.route(qd, kd, w.p, w.kmin, w.budget, grid=w.grid, tile=w.tile)
+    g2 = gpu_lists_to_host(lists2)
+    assert np.array_equal(g["row_ptr"], g2["row_ptr"]) and np.array_equal(g["col_idx"], g2["col_idx"])
+
+    print(f"[parity] config {cid}: attention on GPU", flush=True)
+    o = fva.sparse_attn(qd, kd, vd, lists)
+    o2 = fva.sparse_attn(qd, kd, vd, lists)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2), "attention is not deterministic"
+    rows = _rows_sample(w, lay.Nb, SAMPLE[cid])
+    prec = "fp64" if cid <= 2 else "fp32"
+    err = attention_error(o, qn, kn, vn, lay, g["row_ptr"], g["col_idx"], rows=rows, precision=prec)
+    print(f"[parity] config {cid}: max|o - oracle| = {err:.3e} (tol {TOL[w.dtype]})", flush=True)
+    assert err <= TOL[w.dtype]
+
+
+def _small_case(grid, tile, H, d, dtype, seed, scale=1.0, B=1):
+    N = grid[0] * grid[1] * grid[2]
+    q = tiny_random((B, H, N, d), seed, dtype, scale)
+    k = tiny_random((B, H, N, d), seed + 1, dtype, scale)
+    v = tiny_random((B, H, N, d), seed + 2, dtype)
+    return q, k, v
+
+
+def _run_and_check(dev, q, k, v, grid, tile, p, kmin, budget, tol, chunk=0, strided=False):
+    lay = BlockLayout(grid, tile)
+    qn, kn, vn = (to_numpy(t) for t in (q, k, v))
+    B, H = q.shape[:2]
+    ref = routing.route(qn, kn, lay, p, kmin, budget)
+    if strided:     # views whose token stride is wider than the head dimension
+        d = q.shape[-1]
+        def wide(t):
+            big = torch.zeros(t.shape[:-1] + (d + 64,), dtype=t.dtype, device=dev)
+            big[..., :d] = t.to(dev)
+            return big[..., :d]
+        qd, kd, vd = wide(q), wide(k), wide(v)
+    else:
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    lists = fva.route(qd, kd, p, kmin, budget, grid=grid, tile=tile)
+    g = gpu_lists_to_host(lists)
+    compare_lists(g, ref, p, budget, lay, B, H)
+    out = wide(torch.zeros_like(q)) if strided else torch.empty_like(qd)
+    o = fva.sparse_attn(qd, kd, vd, lists, out=out, chunk_blocks=chunk)
+    assert o.data_ptr() == out.data_ptr()
+    torch.cuda.synchronize()
+    err = attention_error(o, qn, kn, vn, lay, g["row_ptr"], g["col_idx"])
+    assert err <= tol, err
+    return g, o, ref
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("fp32", 128), ("fp32", 64)])
+def test_p_one_is_dense_attention(dev, dtype, d):
+    grid, tile = (3, 20, 20), (2, 8, 8)          # 18 blocks, ragged on every axis
+    q, k, v = _small_case(grid, tile, 2, d, dtype, 50)
+    g, o, _ = _run_and_check(dev, q, k, v, grid, tile, 1.0, 0, ("none", 0.0), TOL[dtype])
+    nb = BlockLayout(grid, tile).Nb
+    assert np.all(np.diff(g["row_ptr"]) == nb)
+    # dense reference: torch CPU scaled_dot_product_attention in float64
+    ref = torch.nn.functional.scaled_dot_product_attention(q.double(), k.double(), v.double())
+    assert (o.double().cpu() - ref).abs().max().item() <= TOL[dtype]
+
+
+@pytest.mark.parametrize("grid,tile,p,kmin,budget", [
+    ((1, 5, 5), (2, 8, 8), 0.9, 4, ("none", 0.0)),            # one partial block: the whole grid
+    ((2, 16, 16), (1, 8, 8), 1e-12, 3, ("none", 0.0)),        # p -> 0+: fixed Top-3
+    ((2, 16, 16), (1, 8, 8), 0.5, 50, ("none", 0.0)),         # floor above the block count
+    ((4, 24, 24), (2, 8, 8), 0.6, 1, ("frac", 1e6)),          # budget capped at every block
+    ((4, 24, 40), (2, 8, 8), 0.8, 2, ("match_max", 0.0)),
+    ((3, 13, 21), (2, 4, 8), 0.7, 2, ("frac", 0.25)),         # 64-token tiles, ragged
+    ((5, 9, 11), (1, 3, 5), 0.9, 1, ("frac", 0.5)),           # 15-token tiles
+])
+def test_edge_cases(dev, grid, tile, p, kmin, budget):
+    q, k, v = _small_case(grid, tile, 3, 128, "bf16", 60, scale=2.0)
+    g, _, _ = _run_and_check(dev, q, k, v, grid, tile, p, kmin, budget, TOL["bf16"])
+    nb = BlockLayout(grid, tile).Nb
+    counts = np.diff(g["row_ptr"])
+    if p < 1e-6:
+        assert np.all(counts == min(nb, max(kmin, 1)))
+    if kmin >= nb or budget[1] >= 1e6:
+        assert np.all(counts == nb)
+
+
+def test_batch_and_strided_views(dev):
+    grid, tile = (3, 16, 24), (2, 8, 8)
+    q, k, v = _small_case(grid, tile, 3, 128, "bf16", 70, scale=2.0, B=2)
+    _run_and_check(dev, q, k, v, grid, tile, 0.85, 2, ("match_max", 0.0), TOL["bf16"], strided=True)
+    qf, kf, vf = _small_case(grid, tile, 2, 64, "fp32", 71, scale=2.0, B=2)
+    _run_and_check(dev, qf, kf, vf, grid, tile, 0.85, 2, ("frac", 0.3), TOL["fp32"], strided=True)
+
+
+@pytest.mark.parametrize("cid,dtype,chunks", [(2, "bf16", (-1, 0, 3, 7)), (1, "fp32", (-1, 0, 3, 1))])
+def test_balancer_does_not_change_results(dev, cid, dtype, chunks):
+    """Splitting rows into work items changes where work runs, not what is kept
+    or computed (within float32 merge rounding)."""
+    w = WORKLOADS[cid]
+    q, k, v, _ = make_inputs(w)
+    lay = BlockLayout(w.grid, w.tile)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    lists = fva.route(qd, kd, w.p, w.kmin, w.budget, grid=w.grid, tile=w.tile)
+    outs = {}
+    for chunk in chunks:
+        st = torch.zeros(fva.stats_bytes(qd, w.grid, w.tile, chunk_blocks=chunk), dtype=torch.uint8, device=dev)
+        outs[chunk] = fva.sparse_attn(qd, kd, vd, lists, chunk_blocks=chunk, stats=st)
+        torch.cuda.synchronize()
+        info, _ = fva.parse_stats(st)
+        R = w.B * w.H * lay.Nb
+        if chunk == -1:
+            assert info.n_items == R and info.n_partials == 0
+        if chunk in (1, 3):
+            assert info.n_partials > 0 and info.n_items > R
+            assert info.chunk_blocks == chunk
+    base = outs[-1].double()
+    rel = 2 ** -7 if dtype == "bf16" else 1e-5          # one bf16 ulp / float32 merge rounding
+    for chunk, o in outs.items():
+        excess = ((o.double() - base).abs() - (base.abs() * rel + 1e-6)).max().item()
+        assert excess <= 0, (chunk, excess)
+    g = gpu_lists_to_host(lists)
+    qn, kn, vn = (to_numpy(t) for t in (q, k, v))
+    for o in outs.values():
+        assert attention_error(o, qn, kn, vn, lay, g["row_ptr"], g["col_idx"]) <= TOL[dtype]
+
+
+def test_empty_problem(dev):
+    q = torch.empty((1, 0, 256, 128), dtype=torch.bfloat16, device=dev)
+    lists = fva.route(q, q, 0.9, 1, None, grid=(4, 8, 8), tile=(1, 8, 8))
+    torch.cuda.synchronize()
+    assert lists.row_ptr.cpu().tolist() == [0]
+    o = fva.sparse_attn(q, q, q, lists)
+    assert o.shape == q.shape
+
+
+def test_stats_and_per_cu_imbalance(dev):
+    w = WORKLOADS[2]
+    q, k, v, _ = make_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    lists = fva.route(qd, kd, w.p, w.kmin, w.budget, grid=w.grid, tile=w.tile)
+    st = torch.zeros(fva.stats_bytes(qd, w.grid, w.tile), dtype=torch.uint8, device=dev)
+    fva.sparse_attn(qd, kd, vd, lists, stats=st)
+    torch.cuda.synchronize()
+    info, ctas = fva.parse_stats(st)
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    assert info.num_ctas == ncu and len(ctas) == ncu
+    assert sum(c.items for c in ctas) == info.n_items
+    assert sum(c.blocks for c in ctas) == info.total_blocks == int(lists.row_ptr[-1].item())
+    assert all(c.t_end >= c.t_start for c in ctas)
+    imb, busy = fva.per_cu_imbalance(ctas, ncu)
+    print(f"\n[stats] ctas={len(ctas)} distinct CU keys={len(busy)} imbalance={imb:.3f}", flush=True)
+    assert imb >= 1.0
