@@ -137,6 +137,18 @@ def make_problem(x: torch.Tensor, grid, tile) -> Problem:
     return Problem(B, H, d, T, Y, X, tt, ty, tx, dt, x.stride(0), x.stride(1), x.stride(2))
 
 
+def block_sizes(grid, tile):
+    """Valid tokens of every block (tile raster order): edge tiles hold fewer."""
+    import numpy as np
+    ext = []
+    for g, t in zip(grid, tile):
+        n = -(-int(g) // int(t))
+        e = np.full(n, int(t), dtype=np.int64)
+        e[-1] = int(g) - (n - 1) * int(t)
+        ext.append(e)
+    return (ext[0][:, None, None] * ext[1][None, :, None] * ext[2][None, None, :]).reshape(-1)
+
+
 def num_blocks(grid, tile, *, B=1, H=1, d=128, dtype=torch.bfloat16) -> int:
     T, Y, X = grid
     p = Problem(B, H, d, T, Y, X, *tile, FVA_BF16 if dtype == torch.bfloat16 else FVA_F32, H * T * Y * X * d,
@@ -326,5 +338,5 @@ def per_cu_imbalance(ctas, num_cus: int):
     return (max(busy.values()) / mean if mean > 0 else 1.0), busy
 
 
-__all__ = ["route", "sparse_attn", "BlockLists", "make_problem", "num_blocks", "load_library", "FvaError",
+__all__ = ["route", "sparse_attn", "BlockLists", "make_problem", "num_blocks", "block_sizes", "load_library", "FvaError",
            "stats_bytes", "parse_stats", "per_cu_imbalance", "lists_from_csr", "EXPORTS", "LIB_PATH"]

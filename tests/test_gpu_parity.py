@@ -162,10 +162,13 @@ def test_balancer_does_not_change_results(dev, cid, dtype, chunks):
         if chunk in (1, 3):
             assert info.n_partials > 0 and info.n_items > R
             assert info.chunk_blocks == chunk
+    # A split row rounds its probabilities to bf16 against each chunk's own
+    # running max, so bf16 results may differ by about one bf16 ulp at the scale
+    # of max(|o|, 1); float32 results only by merge rounding.
     base = outs[-1].double()
-    rel = 2 ** -7 if dtype == "bf16" else 1e-5          # one bf16 ulp / float32 merge rounding
+    rel = 2 ** -7 if dtype == "bf16" else 1e-5
     for chunk, o in outs.items():
-        excess = ((o.double() - base).abs() - (base.abs() * rel + 1e-6)).max().item()
+        excess = ((o.double() - base).abs() - base.abs().clamp(min=1.0) * rel).max().item()
         assert excess <= 0, (chunk, excess)
     g = gpu_lists_to_host(lists)
     qn, kn, vn = (to_numpy(t) for t in (q, k, v))
