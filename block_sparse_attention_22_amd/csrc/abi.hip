@@ -34,6 +34,8 @@ fva_status make_geo(const fva_problem *p, Geo *g) {
     if (p->stride_n < p->head_dim || (p->stride_n % 8) || p->stride_h < 0 || (p->stride_h % 8) ||
         p->stride_b < 0 || (p->stride_b % 8))
         return FVA_ERR_INVALID_ARG;
+    const int64_t elem = (p->dtype == FVA_BF16) ? 2 : 4;
+    if (N * p->stride_n * elem >= INT32_MAX) return FVA_ERR_UNSUPPORTED;   // one head's rows span < 2 GiB
     const int64_t nT = (p->grid_t + p->tile_t - 1) / p->tile_t;
     const int64_t nY = (p->grid_y + p->tile_y - 1) / p->tile_y;
     const int64_t nX = (p->grid_x + p->tile_x - 1) / p->tile_x;
@@ -46,6 +48,7 @@ fva_status make_geo(const fva_problem *p, Geo *g) {
     g->tt = p->tile_t; g->ty = p->tile_y; g->tx = p->tile_x;
     g->nT = (int)nT; g->nY = (int)nY; g->nX = (int)nX;
     g->Nb = (int)Nb;
+    g->N = (int)N;
     g->BH = (int)BH;
     g->sb = p->stride_b; g->sh = p->stride_h; g->sn = p->stride_n;
     g->dtype = p->dtype;
@@ -125,7 +128,7 @@ fva_status attn_sizes(const Geo &g, const fva_attn_options *opts, AttnPlanSizes 
 }
 
 struct AttnWs {
-    size_t tok, bsize, hdr, items, splits, part_o, part_ml, total;
+    size_t tok, bsize, hdr, items, splits, part_o, part_ml, kp, vt, total;
 };
 
 AttnWs attn_layout(const Geo &g, const AttnPlanSizes &s) {
@@ -139,6 +142,8 @@ AttnWs attn_layout(const Geo &g, const AttnPlanSizes &s) {
     w.splits = take((size_t)(s.cap_splits > 0 ? s.cap_splits : 1) * sizeof(SplitRow));
     w.part_o = take((size_t)s.cap_parts * kMaxSlots * g.D * 4);
     w.part_ml = take((size_t)s.cap_parts * kMaxSlots * 2 * 4);
+    w.kp = take(packed_kv_bytes(g));
+    w.vt = take(packed_kv_bytes(g));
     w.total = off;
     return w;
 }
@@ -256,7 +261,8 @@ fva_status fva_sparse_attn(const fva_problem *prob, const void *q, const void *k
     FVA_TRY_HIP(launch_slot_table(g, tok, bsize, s));
     FVA_TRY_HIP(launch_plan(g, lists->row_ptr, chunk, sz.num_ctas, sz.cap_items, sz.cap_parts, hdr, items, splits, s));
     FVA_TRY_HIP(launch_attention(g, q, k, v, o, lists->col_idx, tok, bsize, hdr, items, part_o, part_ml,
-                                 (fva_cta_stat *)stats, sz.num_ctas, s));
+                                 (fva_cta_stat *)stats, (uint16_t *)(W + L.kp), (uint16_t *)(W + L.vt), sz.num_ctas,
+                                 s));
     FVA_TRY_HIP(launch_combine(g, o, tok, bsize, hdr, splits, part_o, part_ml, sz.cap_splits, s));
     return FVA_OK;
 }

@@ -42,6 +42,11 @@ __device__ inline uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// Read-only tables written by earlier launches (lists, block sizes, work
+// items) are read through the constant address space so that wave-uniform
+// reads become scalar loads.
+typedef const int32_t __attribute__((address_space(4))) *cptr_i32;
+
 struct AttnArgs {
     Geo g;
     const void *q, *k, *v;
@@ -92,104 +97,115 @@ __device__ inline int next_item(PlanHeader *hdr, int *s_item) {
 // Swap bits 2 and 3 of a 5-bit MFMA row index: the K row fed to row x.
 __device__ inline int krow_of(int x) { return (x & 0x13) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
-template <int D>
-struct TileRegs {
-    u32x4 k[D / 16];   // K: D/16 passes of 16 B per thread
-    u32x4 v[8];        // V: 8 slots x 16 B per thread (transposed on store)
+// Per-thread share of one key block: 8 consecutive slots (group g8) of one
+// 16-byte chunk c of the head dimension, for K and for V.
+struct TokRegs {
+    int off[8];   // byte offset of the slot's chunk within the head (padding slots repeat a valid token)
+    int n;        // valid tokens of the block
 };
 
-// Global -> registers for key block j (128 slots; missing tokens read as 0).
 template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D> &tr, const int32_t *tj, const uint16_t *kb,
-                                          const uint16_t *vb, int64_t sn) {
-    constexpr int CH = D / 8, RP = 256 / CH, KP = kMaxSlots / RP;
-    const int tid = threadIdx.x;
-    const int c = tid % CH, r0 = tid / CH;
+struct TileRegs {
+    u32x4 k[8];
+    u32x4 v[8];
+};
+
+__device__ __forceinline__ void load_tok(TokRegs &r, const int32_t *tok, const int32_t *bsize, int j, int g8,
+                                         int row_bytes, int cbytes) {
+    const int4 a = *reinterpret_cast<const int4 *>(tok + j * kMaxSlots + 8 * g8);
+    const int4 b = *reinterpret_cast<const int4 *>(tok + j * kMaxSlots + 8 * g8 + 4);
+    r.off[0] = a.x * row_bytes + cbytes; r.off[1] = a.y * row_bytes + cbytes;
+    r.off[2] = a.z * row_bytes + cbytes; r.off[3] = a.w * row_bytes + cbytes;
+    r.off[4] = b.x * row_bytes + cbytes; r.off[5] = b.y * row_bytes + cbytes;
+    r.off[6] = b.z * row_bytes + cbytes; r.off[7] = b.w * row_bytes + cbytes;
+    r.n = ((cptr_i32)bsize)[j];
+}
+
+// Raw buffer descriptor over one head's rows (gfx9 family dword 3).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void *base, int64_t bytes) {
+    const int n = bytes < 0x7fffffffLL ? (int)bytes : 0x7fffffff;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+
+// Global -> registers for one key block; no guards (see the slot table).
+template <int D>
+__device__ __forceinline__ void load_tile(TileRegs<D> &tr, const TokRegs &tk, __amdgpu_buffer_rsrc_t rk,
+                                          __amdgpu_buffer_rsrc_t rv) {
 #pragma unroll
-    for (int p = 0; p < KP; ++p) {
-        const int t = tj[r0 + p * RP];
-        tr.k[p] = (t >= 0) ? *reinterpret_cast<const u32x4 *>(kb + (int64_t)t * sn + c * 8) : u32x4{0, 0, 0, 0};
-    }
-    if (tid < CH * 16) {
-        const int cv = tid >> 4, g8 = tid & 15;
-        const int4 ta = *reinterpret_cast<const int4 *>(tj + 8 * g8);
-        const int4 tb = *reinterpret_cast<const int4 *>(tj + 8 * g8 + 4);
-        const int ts[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-            tr.v[s] = (ts[s] >= 0) ? *reinterpret_cast<const u32x4 *>(vb + (int64_t)ts[s] * sn + cv * 8)
-                                   : u32x4{0, 0, 0, 0};
+    for (int s = 0; s < 8; ++s) {
+        tr.k[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, tk.off[s], 0, 0));
+        tr.v[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, tk.off[s], 0, 0));
     }
 }
 
-// Registers -> LDS.  K: row-major [slot][D], 16-byte chunk c of row s stored
-// at chunk c ^ (s % CH).  V: transposed [D][128 slots], 16-byte group g (8
-// slots) of row dd stored at group g ^ (dd % 16).
+// Position (in 16-byte chunks) of chunk c of K row `slot`: an XOR swizzle that
+// keeps both the tile writes (16 lanes: slots 8*g + s) and the MFMA operand
+// reads (16 lanes: 16 distinct slots of one 32-key subtile) bank-conflict free.
+template <int CH>
+__device__ __forceinline__ int kswz(int slot, int c) { return c ^ ((slot ^ (slot >> 3)) & (CH - 1)); }
+
+// Registers -> LDS.  K: row-major [slot][D] with the swizzle above.
+// V: transposed [D][128 slots], 16-byte group g (8 slots) of row dd stored at
+// group g ^ (dd % 16).
 template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D> &tr, uint16_t *Kt, uint16_t *Vt) {
-    constexpr int CH = D / 8, RP = 256 / CH, KP = kMaxSlots / RP;
-    const int tid = threadIdx.x;
-    const int c = tid % CH, r0 = tid / CH;
+__device__ __forceinline__ void store_tile(const TileRegs<D> &tr, uint16_t *Kt, uint16_t *Vt, int c, int g8) {
+    constexpr int CH = D / 8;
 #pragma unroll
-    for (int p = 0; p < KP; ++p) {
-        const int slot = r0 + p * RP;
-        *reinterpret_cast<u32x4 *>(Kt + slot * D + ((c ^ (slot & (CH - 1))) << 3)) = tr.k[p];
+    for (int s = 0; s < 8; ++s) {
+        const int slot = 8 * g8 + s;
+        *reinterpret_cast<u32x4 *>(Kt + slot * D + (kswz<CH>(slot, c) << 3)) = tr.k[s];
     }
-    if (tid < CH * 16) {
-        const int cv = tid >> 4, g8 = tid & 15;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int dd = 8 * cv + e;
-            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-            u32x4 out;
+    for (int e = 0; e < 8; ++e) {
+        const int dd = 8 * c + e;
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        u32x4 out;
 #pragma unroll
-            for (int w = 0; w < 4; ++w)
-                out[w] = __builtin_amdgcn_perm(tr.v[2 * w + 1][e >> 1], tr.v[2 * w][e >> 1], sel);
-            *reinterpret_cast<u32x4 *>(Vt + dd * kMaxSlots + ((g8 ^ (dd & 15)) << 3)) = out;
-        }
+        for (int w = 0; w < 4; ++w)
+            out[w] = __builtin_amdgcn_perm(tr.v[2 * w + 1][e >> 1], tr.v[2 * w][e >> 1], sel);
+        *reinterpret_cast<u32x4 *>(Vt + dd * kMaxSlots + ((g8 ^ (dd & 15)) << 3)) = out;
     }
 }
 
-// One key block for one wave's 32 queries.
-template <int D>
+// One key block for one wave's 32 queries.  FULL: all 128 slots are valid
+// keys (no masking); otherwise keys at or past n_j get zero probability.
+template <int D, bool FULL>
 __device__ __forceinline__ void compute_tile(const uint16_t *Kt, const uint16_t *Vt, int n_j, const bf16x8 *qf,
                                              f32x16 *acc, float &m_run, float &l_run, float c, int h, int l32) {
     constexpr int CH = D / 8, KS = D / 16, NU = D / 32;
-    const int nsub = (n_j + 31) >> 5;
     const int krow = krow_of(l32);
     f32x16 sacc[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
-        if (t < nsub) {
-            const int slot = 32 * t + krow;
-            const uint16_t *kr = Kt + slot * D;
+    // k-step outer, subtile inner: four independent operand reads in flight
+    // ahead of four independent accumulations.
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kr + (((2 * s + h) ^ (slot & (CH - 1))) << 3));
-                sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[t], 0, 0, 0);
-            }
-        }
-    }
-    if (n_j & 31) {
+    for (int s = 0; s < KS; ++s) {
+        bf16x8 kf[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            if (t == nsub - 1) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = 32 * t + 16 * (r >> 3) + 8 * h + (r & 7);
-                    if (key >= n_j) sacc[t][r] = -INFINITY;
-                }
-            }
+            const int slot = 32 * t + krow;
+            kf[t] = *reinterpret_cast<const bf16x8 *>(Kt + slot * D + (kswz<CH>(slot, 2 * s + h) << 3));
         }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t], qf[s], sacc[t], 0, 0, 0);
+    }
+    if (!FULL) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = 32 * t + 16 * (r >> 3) + 8 * h + (r & 7);
+                if (key >= n_j) sacc[t][r] = -INFINITY;
+            }
     }
     float mloc = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-        if (t < nsub)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[t][r]);
+        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[t][r]);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
     const float mnew = fmaxf(m_run, mloc);
     const float alpha = __builtin_amdgcn_exp2f((m_run - mnew) * c);
@@ -205,29 +221,26 @@ __device__ __forceinline__ void compute_tile(const uint16_t *Kt, const uint16_t 
     bf16x8 pf[8];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        if (t < nsub) {
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
+        for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[t][8 * hf + e], c, -mc));
-                    l_run += pv;
-                    pf[2 * t + hf][e] = (__bf16)pv;
-                }
+            for (int e = 0; e < 8; ++e) {
+                const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[t][8 * hf + e], c, -mc));
+                l_run += pv;
+                pf[2 * t + hf][e] = (__bf16)pv;
             }
         }
     }
 #pragma unroll
     for (int sg = 0; sg < 8; ++sg) {
-        if (sg < 2 * nsub) {
+        bf16x8 vf[NU];
 #pragma unroll
-            for (int u = 0; u < NU; ++u) {
-                const int dd = 32 * u + l32;
-                const bf16x8 vf =
-                    *reinterpret_cast<const bf16x8 *>(Vt + dd * kMaxSlots + (((2 * sg + h) ^ (dd & 15)) << 3));
-                acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[sg], acc[u], 0, 0, 0);
-            }
+        for (int u = 0; u < NU; ++u) {
+            const int dd = 32 * u + l32;
+            vf[u] = *reinterpret_cast<const bf16x8 *>(Vt + dd * kMaxSlots + (((2 * sg + h) ^ (dd & 15)) << 3));
         }
+#pragma unroll
+        for (int u = 0; u < NU; ++u) acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u], pf[sg], acc[u], 0, 0, 0);
     }
 }
 
@@ -239,6 +252,10 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
     __shared__ int s_item;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    // Tile loading role: chunk lc of the head dimension for slots 8*g8..8*g8+7
+    // (all 256 threads for D = 128, the first 128 for D = 64).
+    const int lc = tid >> 4, g8 = tid & 15;
+    const bool ldr = tid < (D / 8) * 16;
     const Geo &g = a.g;
     const float c = a.scale_log2;
     const uint64_t t0 = wall_clock64();
@@ -250,12 +267,19 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
     uint16_t *O = static_cast<uint16_t *>(a.o);
 
     for (;;) {
-        const int it = next_item(a.hdr, &s_item);
+        // Work-item fields are wave-uniform: keep them in scalar registers so
+        // the per-block index reads below are scalar loads (lgkmcnt), not
+        // vector loads that would queue behind the K/V data loads (vmcnt).
+        const int it = __builtin_amdgcn_readfirstlane(next_item(a.hdr, &s_item));
         if (it >= n_items) break;
-        const WorkItem wi = a.items[it];
+        WorkItem wi;
+        {
+            const cptr_i32 ip = (cptr_i32)a.items + 4 * it;
+            wi.row = ip[0]; wi.kb_begin = ip[1]; wi.kb_end = ip[2]; wi.part = ip[3];
+        }
         const int bh = wi.row / g.Nb, i = wi.row - (wi.row / g.Nb) * g.Nb;
         const int64_t boff = (int64_t)(bh / g.H) * g.sb + (int64_t)(bh % g.H) * g.sh;
-        const int n_i = a.bsize[i];
+        const int n_i = ((cptr_i32)a.bsize)[i];
         const bool active = (w * 32) < n_i;
         const int qslot = w * 32 + l32;
         const bool qvalid = qslot < n_i;
@@ -263,8 +287,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
         bf16x8 qf[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            u32x4 raw = qvalid ? *reinterpret_cast<const u32x4 *>(Q + boff + (int64_t)qtok * g.sn + 16 * s + 8 * h)
-                               : u32x4{0, 0, 0, 0};
+            const u32x4 raw = *reinterpret_cast<const u32x4 *>(Q + boff + (int64_t)qtok * g.sn + 16 * s + 8 * h);
             qf[s] = __builtin_bit_cast(bf16x8, raw);
         }
         f32x16 acc[NU];
@@ -274,24 +297,36 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
             for (int r = 0; r < 16; ++r) acc[u][r] = 0.f;
         float m_run = -INFINITY, l_run = 0.f;
         const int nkb = wi.kb_end - wi.kb_begin;
+        const cptr_i32 cols = (cptr_i32)a.col_idx + wi.kb_begin;
         if (nkb > 0) {
+            // Software pipeline: token indices two blocks ahead, K/V data one
+            // block ahead (registers), LDS double buffer for the block in use.
+            const int64_t head_bytes = (int64_t)g.N * g.sn * 2;
+            const __amdgpu_buffer_rsrc_t rk = head_rsrc(K + boff, head_bytes);
+            const __amdgpu_buffer_rsrc_t rv = head_rsrc(V + boff, head_bytes);
+            const int row_bytes = (int)(g.sn * 2), cbytes = lc * 16;
+            TokRegs tnext;
             TileRegs<D> tr;
-            int j = a.col_idx[wi.kb_begin];
-            load_tile<D>(tr, a.tok + j * kMaxSlots, K + boff, V + boff, g.sn);
-            store_tile<D>(tr, Ks[0], Vs[0]);
+            load_tok(tnext, a.tok, a.bsize, cols[0], g8, row_bytes, cbytes);
+            if (ldr) load_tile<D>(tr, tnext, rk, rv);
+            int n_cur = tnext.n;
+            if (nkb > 1) load_tok(tnext, a.tok, a.bsize, cols[1], g8, row_bytes, cbytes);
+            if (ldr) store_tile<D>(tr, Ks[0], Vs[0], lc, g8);
             __syncthreads();
             for (int jj = 0; jj < nkb; ++jj) {
                 const int buf = jj & 1;
-                const int n_j = a.bsize[j];
-                int jn = j;
-                if (jj + 1 < nkb) {
-                    jn = a.col_idx[wi.kb_begin + jj + 1];
-                    load_tile<D>(tr, a.tok + jn * kMaxSlots, K + boff, V + boff, g.sn);
+                const int n_next = tnext.n;
+                if (jj + 1 < nkb && ldr) load_tile<D>(tr, tnext, rk, rv);
+                if (jj + 2 < nkb) load_tok(tnext, a.tok, a.bsize, cols[jj + 2], g8, row_bytes, cbytes);
+                if (active) {
+                    if (n_cur == kMaxSlots)
+                        compute_tile<D, true>(Ks[buf], Vs[buf], n_cur, qf, acc, m_run, l_run, c, h, l32);
+                    else
+                        compute_tile<D, false>(Ks[buf], Vs[buf], n_cur, qf, acc, m_run, l_run, c, h, l32);
                 }
-                if (active) compute_tile<D>(Ks[buf], Vs[buf], n_j, qf, acc, m_run, l_run, c, h, l32);
-                if (jj + 1 < nkb) store_tile<D>(tr, Ks[buf ^ 1], Vs[buf ^ 1]);
+                if (jj + 1 < nkb && ldr) store_tile<D>(tr, Ks[buf ^ 1], Vs[buf ^ 1], lc, g8);
                 __syncthreads();
-                j = jn;
+                n_cur = n_next;
             }
         }
         const float l = l_run + __shfl_xor(l_run, 32, 64);
@@ -330,6 +365,283 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
         blocks_done += nkb;
     }
     write_stats(a, t0, n_done, blocks_done);
+}
+
+// ----------------------------------------------------------------------
+// Head dimension 128, bf16: the production kernel.
+//
+// Two workgroups per CU (two waves per SIMD), so one wave's softmax overlaps
+// the other wave's matrix work.  Keys are consumed in 64-key half blocks held
+// in a two-stage LDS ring (2 x (16 KB K + 16 KB V^T) per workgroup), filled by
+// LDS-DMA buffer loads issued one half block ahead from the block-major K and
+// V^T copies that pack_kv_kernel writes (so every DMA address is scalar plus
+// lane arithmetic, with no per-lane index loads).  The running row max is only raised when it grows by
+// more than 8 (log2 units), which skips most rescales of the accumulator and
+// keeps probabilities below 2^8 (exact: the same offset is used in numerator
+// and denominator).
+constexpr int kHalf = 64;                        // keys per half block
+constexpr int kHalfBytes = kHalf * 128 * 2;      // 16 KB: K or V^T of one half block
+constexpr float kLazyMax = 8.0f;
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// K half block: [64 slots][128] bf16, 16-byte chunk c of row s at c ^ f(s).
+__device__ __forceinline__ int kpos128(int slot, int c) { return c ^ ((slot ^ (slot >> 3)) & 15); }
+// V^T half block: [128 dd][64 slots] bf16, 8-slot group g of row dd at g ^ ((dd >> 1) & 7).
+__device__ __forceinline__ int vpos128(int dd, int g) { return g ^ ((dd >> 1) & 7); }
+
+// Issue the LDS-DMA loads of one half block of packed block j: 4 + 4 wave
+// instructions of 1 KB; each lane fetches the 16-byte chunk that the swizzle
+// places at its LDS position.
+__device__ __forceinline__ void dma_half(uint16_t *Kst, uint16_t *Vst, __amdgpu_buffer_rsrc_t rkp,
+                                         __amdgpu_buffer_rsrc_t rvt, int j, int half, int w, int lane) {
+    const int blk = j * kMaxSlots * 256;              // bytes of one packed block (K or V^T)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int seg = 4 * w + i;                    // 1 KB segment: 4 K rows / 8 V^T rows
+        const int slot = 4 * seg + (lane >> 4);       // K row within the half
+        const int ck = (lane & 15) ^ ((slot ^ (slot >> 3)) & 15);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rkp, (lds_ptr_t)(Kst + seg * 512), 16,
+                                                 blk + (kHalf * half + slot) * 256 + ck * 16, 0, 0, 0);
+        const int dd = 8 * seg + (lane >> 3);
+        const int gv = (lane & 7) ^ ((dd >> 1) & 7);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rvt, (lds_ptr_t)(Vst + seg * 512), 16,
+                                                 blk + dd * 256 + (kHalf * half + 8 * gv) * 2, 0, 0, 0);
+    }
+}
+
+// One 64-key half block for one wave's 32 queries; keys at or past nvalid get
+// zero probability.  `lane` is made opaque so that the LDS addresses below are
+// recomputed per call rather than hoisted (and kept live) across the loop.
+__device__ __forceinline__ void half_tile(const uint16_t *Kt, const uint16_t *Vt, int nvalid, const bf16x8 *qf,
+                                          f32x16 *acc, float &m_run, float &l_run, float c, int lane) {
+    asm volatile("" : "+v"(lane));
+    const int h = lane >> 5, l32 = lane & 31;
+    const int krow = krow_of(l32);
+    f32x16 sacc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        bf16x8 kf[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int slot = 32 * t + krow;
+            kf[t] = *reinterpret_cast<const bf16x8 *>(Kt + slot * 128 + (kpos128(slot, 2 * s + h) << 3));
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t], qf[s], sacc[t], 0, 0, 0);
+    }
+    if (nvalid < kHalf) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = 32 * t + 16 * (r >> 3) + 8 * h + (r & 7);
+                if (key >= nvalid) sacc[t][r] = -INFINITY;
+            }
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[t][r]);
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * c;
+    if (__any(mloc > m_run + kLazyMax)) {
+        const float mnew = fmaxf(m_run, mloc);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+        m_run = mnew;
+        l_run *= alpha;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[u][r] *= alpha;
+    }
+    bf16x8 pf[4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[t][8 * hf + e], c, -m_run));
+                l_run += pv;
+                pf[2 * t + hf][e] = (__bf16)pv;
+            }
+#pragma unroll
+    for (int sg = 0; sg < 4; ++sg) {
+        bf16x8 vf[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int dd = 32 * u + l32;
+            vf[u] = *reinterpret_cast<const bf16x8 *>(Vt + dd * kHalf + (vpos128(dd, 2 * sg + h) << 3));
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u], pf[sg], acc[u], 0, 0, 0);
+    }
+}
+
+__global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, const uint16_t *Kp_all,
+                                                                  const uint16_t *Vt_all) {
+    // Two LDS stages as distinct objects, so the compiler can see that the
+    // DMA into one stage does not alias the reads of the other.
+    __shared__ __attribute__((aligned(16))) uint16_t Ks0[kHalf * 128];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs0[kHalf * 128];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks1[kHalf * 128];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs1[kHalf * 128];
+    __shared__ int s_item;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    const Geo &g = a.g;
+    const float c = a.scale_log2;
+    const uint64_t t0 = wall_clock64();
+    uint32_t n_done = 0, blocks_done = 0;
+    const int n_items = a.hdr->info.n_items;
+    const uint16_t *Q = static_cast<const uint16_t *>(a.q);
+    const uint16_t *K = static_cast<const uint16_t *>(a.k);
+    uint16_t *O = static_cast<uint16_t *>(a.o);
+    const int row_bytes = (int)(g.sn * 2);
+
+    for (;;) {
+        const int it = __builtin_amdgcn_readfirstlane(next_item(a.hdr, &s_item));
+        if (it >= n_items) break;
+        WorkItem wi;
+        {
+            const cptr_i32 ip = (cptr_i32)a.items + 4 * it;
+            wi.row = ip[0]; wi.kb_begin = ip[1]; wi.kb_end = ip[2]; wi.part = ip[3];
+        }
+        const int bh = wi.row / g.Nb, i = wi.row - (wi.row / g.Nb) * g.Nb;
+        const int64_t boff = (int64_t)(bh / g.H) * g.sb + (int64_t)(bh % g.H) * g.sh;
+        const int n_i = ((cptr_i32)a.bsize)[i];
+        const bool active = (w * 32) < n_i;
+        const int qslot = w * 32 + l32;
+        const bool qvalid = qslot < n_i;
+        const int qtok = a.tok[i * kMaxSlots + qslot];
+        bf16x8 qf[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const u32x4 raw = *reinterpret_cast<const u32x4 *>(Q + boff + (int64_t)qtok * g.sn + 16 * s + 8 * h);
+            qf[s] = __builtin_bit_cast(bf16x8, raw);
+        }
+        f32x16 acc[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[u][r] = 0.f;
+        float m_run = -INFINITY, l_run = 0.f;
+        const int nkb = wi.kb_end - wi.kb_begin;
+        const cptr_i32 cols = (cptr_i32)a.col_idx + wi.kb_begin;
+        if (nkb > 0) {
+            const int64_t head_packed = (int64_t)bh * g.Nb * kMaxSlots * 128;
+            const __amdgpu_buffer_rsrc_t rkp = head_rsrc(Kp_all + head_packed, (int64_t)g.Nb * kMaxSlots * 256);
+            const __amdgpu_buffer_rsrc_t rvt = head_rsrc(Vt_all + head_packed, (int64_t)g.Nb * kMaxSlots * 256);
+            const cptr_i32 bsz = (cptr_i32)a.bsize;
+            // Half-block stream over the kept blocks: block jj (index j, nj
+            // tokens), half hh.  Block indices are read two blocks ahead and
+            // sizes one block ahead (scalar loads), K/V one half ahead (DMA).
+            int jj = 0, hh = 0;
+            int j = cols[0], nj = bsz[j];
+            int j1 = (nkb > 1) ? cols[1] : 0;
+            int n1 = (nkb > 1) ? bsz[j1] : 0;
+            int j2 = (nkb > 2) ? cols[2] : 0;
+            dma_half(Ks0, Vs0, rkp, rvt, j, 0, w, lane);
+            // One step of the stream: wait for the current stage, start the
+            // DMA of the next half into the other stage, compute the current.
+            // Unrolled by two so both stages are fixed objects in each step.
+            auto step = [&](uint16_t *Kc, uint16_t *Vc, uint16_t *Kn, uint16_t *Vn) -> bool {
+                const bool same = (hh + 1) * kHalf < nj;
+                const int jn = same ? jj : jj + 1;
+                const int hn = same ? hh + 1 : 0;
+                const int jnext = same ? j : j1;
+                __builtin_amdgcn_s_waitcnt(0x0f70);       // vmcnt(0): this wave's DMA for the current half landed
+                __syncthreads();                          // ... and every wave's; the other stage is free again
+                if (jn < nkb) dma_half(Kn, Vn, rkp, rvt, jnext, hn, w, lane);
+                if (active) half_tile(Kc, Vc, nj - hh * kHalf, qf, acc, m_run, l_run, c, lane);
+                if (jn >= nkb) return false;
+                if (!same) {
+                    jj = jn;
+                    j = j1; nj = n1;
+                    if (jj + 1 < nkb) { j1 = j2; n1 = bsz[j2]; }
+                    if (jj + 2 < nkb) j2 = cols[jj + 2];
+                }
+                hh = hn;
+                return true;
+            };
+            while (step(Ks0, Vs0, Ks1, Vs1) && step(Ks1, Vs1, Ks0, Vs0)) {
+            }
+            __syncthreads();       // all waves done with both stages before the next item's DMA
+        }
+        const float l = l_run + __shfl_xor(l_run, 32, 64);
+        if (active && qvalid) {
+            if (wi.part < 0) {
+                const float inv = (l > 0.f) ? 1.f / l : 0.f;
+                uint16_t *orow = O + boff + (int64_t)qtok * g.sn;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg) {
+                        const int dd = 32 * u + 8 * rg + 4 * h;
+                        *reinterpret_cast<uint2 *>(orow + dd) =
+                            make_uint2(pack_bf16(acc[u][4 * rg] * inv, acc[u][4 * rg + 1] * inv),
+                                       pack_bf16(acc[u][4 * rg + 2] * inv, acc[u][4 * rg + 3] * inv));
+                    }
+            } else {
+                float *po = a.part_o + ((int64_t)wi.part * kMaxSlots + qslot) * 128;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg) {
+                        const int dd = 32 * u + 8 * rg + 4 * h;
+                        *reinterpret_cast<float4 *>(po + dd) =
+                            make_float4(acc[u][4 * rg], acc[u][4 * rg + 1], acc[u][4 * rg + 2], acc[u][4 * rg + 3]);
+                    }
+                if (h == 0) {
+                    float *pm = a.part_ml + ((int64_t)wi.part * kMaxSlots + qslot) * 2;
+                    pm[0] = m_run;
+                    pm[1] = l;
+                }
+            }
+        }
+        ++n_done;
+        blocks_done += nkb;
+    }
+    write_stats(a, t0, n_done, blocks_done);
+}
+
+// Block-major copies for the d=128 kernel, one workgroup per (block,
+// batch*head): Kp[(bh*Nb + j)*128 + slot][128] and Vt[(bh*Nb + j)*128 + dd][128
+// slots], slots past the block's tokens zero.  Each thread moves 8 slots of one
+// 16-byte chunk and transposes its 8x8 V tile in registers.
+__global__ __launch_bounds__(256) void pack_kv_kernel(Geo g, const uint16_t *K, const uint16_t *V,
+                                                      const int32_t *tok, const int32_t *bsize, uint16_t *Kp,
+                                                      uint16_t *Vt) {
+    const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+    const int cv = tid >> 4, g8 = tid & 15;
+    const int n = bsize[j];
+    const int64_t hoff = (int64_t)(bh / g.H) * g.sb + (int64_t)(bh % g.H) * g.sh;
+    const int64_t pblk = ((int64_t)bh * g.Nb + j) * kMaxSlots * 128;
+    u32x4 in[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const int slot = 8 * g8 + s;
+        const int t = tok[j * kMaxSlots + slot];
+        const int64_t src = hoff + (int64_t)t * g.sn + cv * 8;
+        u32x4 kx = *reinterpret_cast<const u32x4 *>(K + src);
+        in[s] = *reinterpret_cast<const u32x4 *>(V + src);
+        if (slot >= n) { kx = u32x4{0, 0, 0, 0}; in[s] = u32x4{0, 0, 0, 0}; }
+        *reinterpret_cast<u32x4 *>(Kp + pblk + slot * 128 + cv * 8) = kx;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int dd = 8 * cv + e;
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        u32x4 o;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) o[w] = __builtin_amdgcn_perm(in[2 * w + 1][e >> 1], in[2 * w][e >> 1], sel);
+        *reinterpret_cast<u32x4 *>(Vt + pblk + dd * kMaxSlots + 8 * g8) = o;
+    }
 }
 
 // Float32 path: one thread per query slot, K/V tiles of one key block in LDS.
@@ -556,7 +868,11 @@ __global__ __launch_bounds__(256) void combine_kernel(Geo g, OutT *O, const int3
 }  // namespace
 
 // ---------------------------------------------------------------- launches
-int attention_ctas_per_cu(const Geo &) { return 1; }
+int attention_ctas_per_cu(const Geo &g) { return (g.dtype == FVA_BF16 && g.D == 128) ? 2 : 1; }
+
+size_t packed_kv_bytes(const Geo &g) {
+    return (g.dtype == FVA_BF16 && g.D == 128) ? (size_t)g.BH * g.Nb * kMaxSlots * 128 * 2 : 0;
+}
 
 hipError_t launch_plan(const Geo &g, const int32_t *row_ptr, int chunk_mode, int num_ctas, int cap_items,
                        int cap_parts, PlanHeader *hdr, WorkItem *items, SplitRow *splits, hipStream_t s) {
@@ -568,7 +884,7 @@ hipError_t launch_plan(const Geo &g, const int32_t *row_ptr, int chunk_mode, int
 hipError_t launch_attention(const Geo &g, const void *q, const void *k, const void *v, void *o,
                             const int32_t *col_idx, const int32_t *tok, const int32_t *bsize, PlanHeader *hdr,
                             const WorkItem *items, float *part_o, float *part_ml, fva_cta_stat *stats,
-                            int num_ctas, hipStream_t s) {
+                            uint16_t *kp, uint16_t *vt, int num_ctas, hipStream_t s) {
     AttnArgs a;
     a.g = g;
     a.q = q; a.k = k; a.v = v; a.o = o;
@@ -578,8 +894,15 @@ hipError_t launch_attention(const Geo &g, const void *q, const void *k, const vo
     a.stats = stats;
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.D));
     if (g.dtype == FVA_BF16) {
-        if (g.D == 128) hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(num_ctas), dim3(256), 0, s, a);
-        else hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(num_ctas), dim3(256), 0, s, a);
+        if (g.D == 128) {
+            hipLaunchKernelGGL(pack_kv_kernel, dim3(g.Nb, g.BH), dim3(256), 0, s, g, (const uint16_t *)k,
+                               (const uint16_t *)v, tok, bsize, kp, vt);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(attn_bf16_d128_kernel, dim3(num_ctas), dim3(256), 0, s, a, kp, vt);
+        } else {
+            hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(num_ctas), dim3(256), 0, s, a);
+        }
     } else {
         if (g.D == 128) hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(num_ctas), dim3(kMaxSlots), 0, s, a);
         else hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(num_ctas), dim3(kMaxSlots), 0, s, a);

@@ -17,6 +17,7 @@ struct Geo {
     int tt, ty, tx;
     int nT, nY, nX;
     int Nb;          // Nq = Nk
+    int N;           // tokens per (batch, head)
     int BH;
     int64_t sb, sh, sn;
     int dtype;
@@ -63,7 +64,8 @@ hipError_t launch_plan(const Geo &g, const int32_t *row_ptr, int chunk_mode, int
 hipError_t launch_attention(const Geo &g, const void *q, const void *k, const void *v, void *o,
                             const int32_t *col_idx, const int32_t *tok, const int32_t *bsize,
                             PlanHeader *hdr, const WorkItem *items, float *part_o, float *part_ml,
-                            fva_cta_stat *stats, int num_ctas, hipStream_t s);
+                            fva_cta_stat *stats, uint16_t *kp, uint16_t *vt, int num_ctas, hipStream_t s);
+size_t packed_kv_bytes(const Geo &g);
 hipError_t launch_combine(const Geo &g, void *o, const int32_t *tok, const int32_t *bsize,
                           const PlanHeader *hdr, const SplitRow *splits, const float *part_o,
                           const float *part_ml, int cap_splits, hipStream_t s);

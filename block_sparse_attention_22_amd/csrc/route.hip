@@ -85,9 +85,11 @@ __device__ inline T block_exclusive_scan(T x, T *tmp, T *total) {
 }
 
 // ------------------------------------------------------------ slot table
-// tok[b*128 + r] = token index of slot r of block b, or -1 past the block's
-// valid tokens; slots enumerate the tile's existing tokens in (t, y, x)
-// raster order so an edge tile's tokens are packed at the front.
+// tok[b*128 + r] = token index of slot r of block b.  Slots enumerate the
+// tile's existing tokens in (t, y, x) raster order, so an edge tile's tokens
+// are packed at the front; slots at or past bsize[b] repeat the block's first
+// token so that loads never need a guard (their scores are masked and their
+// values multiplied by zero probability).
 __global__ __launch_bounds__(kMaxSlots) void slot_table_kernel(Geo g, int32_t *tok, int32_t *bsize) {
     const int b = blockIdx.x, r = threadIdx.x;
     const int it = b / (g.nY * g.nX), iy = (b / g.nX) % g.nY, ix = b % g.nX;
@@ -95,12 +97,9 @@ __global__ __launch_bounds__(kMaxSlots) void slot_table_kernel(Geo g, int32_t *t
     const int ey = min(g.ty, g.Y - iy * g.ty);
     const int ex = min(g.tx, g.X - ix * g.tx);
     const int n = et * ey * ex;
-    int t = -1;
-    if (r < n) {
-        const int dt = r / (ey * ex), rem = r % (ey * ex), dy = rem / ex, dx = rem % ex;
-        t = ((it * g.tt + dt) * g.Y + (iy * g.ty + dy)) * g.X + (ix * g.tx + dx);
-    }
-    tok[b * kMaxSlots + r] = t;
+    const int rr = (r < n) ? r : 0;
+    const int dt = rr / (ey * ex), rem = rr % (ey * ex), dy = rem / ex, dx = rem % ex;
+    tok[b * kMaxSlots + r] = ((it * g.tt + dt) * g.Y + (iy * g.ty + dy)) * g.X + (ix * g.tx + dx);
     if (r == 0) bsize[b] = n;
 }
 
