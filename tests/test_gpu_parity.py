@@ -163,12 +163,17 @@ def test_balancer_does_not_change_results(dev, cid, dtype, chunks):
             assert info.n_partials > 0 and info.n_items > R
             assert info.chunk_blocks == chunk
     # A split row rounds its probabilities to bf16 against each chunk's own
-    # running max, so bf16 results may differ by about one bf16 ulp at the scale
-    # of max(|o|, 1); float32 results only by merge rounding.
+    # running max, so two bf16 results differ by at most the probability
+    # rounding (relative 2^-9 per term, so 2^-9 * max|v| on the output) plus
+    # one output ulp; float32 results only by merge rounding.
     base = outs[-1].double()
-    rel = 2 ** -7 if dtype == "bf16" else 1e-5
+    vmax = v.abs().max().item()
     for chunk, o in outs.items():
-        excess = ((o.double() - base).abs() - base.abs().clamp(min=1.0) * rel).max().item()
+        if dtype == "bf16":
+            bound = 2 ** -9 * vmax + base.abs().clamp(min=1.0) * 2 ** -7
+        else:
+            bound = base.abs().clamp(min=1.0) * 1e-5
+        excess = ((o.double() - base).abs() - bound).max().item()
         assert excess <= 0, (chunk, excess)
     g = gpu_lists_to_host(lists)
     qn, kn, vn = (to_numpy(t) for t in (q, k, v))
@@ -195,7 +200,7 @@ def test_stats_and_per_cu_imbalance(dev):
     torch.cuda.synchronize()
     info, ctas = fva.parse_stats(st)
     ncu = torch.cuda.get_device_properties(dev).multi_processor_count
-    assert info.num_ctas == ncu and len(ctas) == ncu
+    assert info.num_ctas in (ncu, 2 * ncu) and len(ctas) == info.num_ctas     # 1 or 2 workgroups per CU
     assert sum(c.items for c in ctas) == info.n_items
     assert sum(c.blocks for c in ctas) == info.total_blocks == int(lists.row_ptr[-1].item())
     assert all(c.t_end >= c.t_start for c in ctas)
