@@ -123,6 +123,8 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -148,6 +150,15 @@ def main():
     def step():
         fva.route(qd, kd, w.p, w.kmin, w.budget, grid=w.grid, tile=w.tile, out=lists)
         fva.sparse_attn(qd, kd, vd, lists, out=out)
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: {args.copy_calibration_mib} MiB read + {args.copy_calibration_mib} MiB written")
+        del src, dst
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):

@@ -410,14 +410,36 @@ __device__ __forceinline__ void dma_half(uint16_t *Kst, uint16_t *Vst, __amdgpu_
     }
 }
 
-// One 64-key half block for one wave's 32 queries; keys at or past nvalid get
-// zero probability.  `lane` is made opaque so that the LDS addresses below are
-// recomputed per call rather than hoisted (and kept live) across the loop.
-__device__ __forceinline__ void half_tile(const uint16_t *Kt, const uint16_t *Vt, int nvalid, const bf16x8 *qf,
-                                          f32x16 *acc, float &m_run, float &l_run, float c, int lane) {
-    asm volatile("" : "+v"(lane));
+// Per-lane LDS byte offsets of the MFMA operand reads, fixed for the whole
+// kernel.  K: the subtile t and the stage add immediates; the chunk order of
+// k-step s for subtile 1 is that of step s ^ 2 for subtile 0 (the swizzle of
+// row 32 + x is the swizzle of row x with bit 2 flipped).  V^T: the 32-row
+// tile u adds an immediate.
+struct OperandAddr {
+    uint32_t k[8];    // K row krow(l32), chunk for k-step s, subtile 0
+    uint32_t v[4];    // V^T row l32, group for key step sg
+};
+
+__device__ __forceinline__ OperandAddr operand_addr(int lane) {
+    OperandAddr o;
     const int h = lane >> 5, l32 = lane & 31;
     const int krow = krow_of(l32);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) o.k[s] = (uint32_t)(krow * 256 + (kpos128(krow, 2 * s + h) << 4));
+#pragma unroll
+    for (int sg = 0; sg < 4; ++sg) o.v[sg] = (uint32_t)(l32 * kHalf * 2 + (vpos128(l32, 2 * sg + h) << 4));
+    return o;
+}
+
+__device__ __forceinline__ bf16x8 lds_read16(const uint16_t *base, uint32_t byte_off) {
+    return *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const char *>(base) + byte_off);
+}
+
+// One 64-key half block for one wave's 32 queries; keys at or past nvalid get
+// zero probability.
+__device__ __forceinline__ void half_tile(const uint16_t *Kt, const uint16_t *Vt, int nvalid, const bf16x8 *qf,
+                                          f32x16 *acc, float &m_run, float &l_run, float c, int h,
+                                          const OperandAddr &oa) {
     f32x16 sacc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -425,14 +447,10 @@ __device__ __forceinline__ void half_tile(const uint16_t *Kt, const uint16_t *Vt
         for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-        bf16x8 kf[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int slot = 32 * t + krow;
-            kf[t] = *reinterpret_cast<const bf16x8 *>(Kt + slot * 128 + (kpos128(slot, 2 * s + h) << 3));
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t], qf[s], sacc[t], 0, 0, 0);
+        const bf16x8 k0 = lds_read16(Kt, oa.k[s]);
+        const bf16x8 k1 = lds_read16(Kt + 32 * 128, oa.k[s ^ 2]);
+        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], sacc[0], 0, 0, 0);
+        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], sacc[1], 0, 0, 0);
     }
     if (nvalid < kHalf) {
 #pragma unroll
@@ -474,10 +492,7 @@ __device__ __forceinline__ void half_tile(const uint16_t *Kt, const uint16_t *Vt
     for (int sg = 0; sg < 4; ++sg) {
         bf16x8 vf[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int dd = 32 * u + l32;
-            vf[u] = *reinterpret_cast<const bf16x8 *>(Vt + dd * kHalf + (vpos128(dd, 2 * sg + h) << 3));
-        }
+        for (int u = 0; u < 4; ++u) vf[u] = lds_read16(Vt + u * 32 * kHalf, oa.v[sg]);
 #pragma unroll
         for (int u = 0; u < 4; ++u) acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u], pf[sg], acc[u], 0, 0, 0);
     }
@@ -502,7 +517,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
     const uint16_t *Q = static_cast<const uint16_t *>(a.q);
     const uint16_t *K = static_cast<const uint16_t *>(a.k);
     uint16_t *O = static_cast<uint16_t *>(a.o);
-    const int row_bytes = (int)(g.sn * 2);
+    const OperandAddr oa = operand_addr(lane);
 
     for (;;) {
         const int it = __builtin_amdgcn_readfirstlane(next_item(a.hdr, &s_item));
@@ -558,7 +573,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
                 __builtin_amdgcn_s_waitcnt(0x0f70);       // vmcnt(0): this wave's DMA for the current half landed
                 __syncthreads();                          // ... and every wave's; the other stage is free again
                 if (jn < nkb) dma_half(Kn, Vn, rkp, rvt, jnext, hn, w, lane);
-                if (active) half_tile(Kc, Vc, nj - hh * kHalf, qf, acc, m_run, l_run, c, lane);
+                if (active) half_tile(Kc, Vc, nj - hh * kHalf, qf, acc, m_run, l_run, c, h, oa);
                 if (jn >= nkb) return false;
                 if (!same) {
                     jj = jn;
@@ -622,16 +637,23 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(Geo g, const uint16_t *K, 
     const int n = bsize[j];
     const int64_t hoff = (int64_t)(bh / g.H) * g.sb + (int64_t)(bh % g.H) * g.sh;
     const int64_t pblk = ((int64_t)bh * g.Nb + j) * kMaxSlots * 128;
+    // K: 16 lanes move one 256-byte row (coalesced reads and writes).
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const int slot = (tid >> 4) + 16 * m, ck = tid & 15;
+        const int t = tok[j * kMaxSlots + slot];
+        u32x4 kx = *reinterpret_cast<const u32x4 *>(K + hoff + (int64_t)t * g.sn + ck * 8);
+        if (slot >= n) kx = u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4 *>(Kp + pblk + slot * 128 + ck * 8) = kx;
+    }
+    // V: 8 slots x one 16-byte chunk per thread, transposed in registers.
     u32x4 in[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
         const int slot = 8 * g8 + s;
         const int t = tok[j * kMaxSlots + slot];
-        const int64_t src = hoff + (int64_t)t * g.sn + cv * 8;
-        u32x4 kx = *reinterpret_cast<const u32x4 *>(K + src);
-        in[s] = *reinterpret_cast<const u32x4 *>(V + src);
-        if (slot >= n) { kx = u32x4{0, 0, 0, 0}; in[s] = u32x4{0, 0, 0, 0}; }
-        *reinterpret_cast<u32x4 *>(Kp + pblk + slot * 128 + cv * 8) = kx;
+        in[s] = *reinterpret_cast<const u32x4 *>(V + hoff + (int64_t)t * g.sn + cv * 8);
+        if (slot >= n) in[s] = u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
