@@ -48,7 +48,7 @@ class ListsC(ctypes.Structure):
 
 class AttnOptions(ctypes.Structure):
     _fields_ = [("chunk_blocks", ctypes.c_int32), ("num_ctas", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 6)]
+                ("reserved", ctypes.c_int32 * 2), ("kernel_events", ctypes.c_void_p * 2)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -243,10 +243,23 @@ def route(q: torch.Tensor, k: torch.Tensor, p: float, kmin: int, budget=None, *,
     return out
 
 
-def attn_options(chunk_blocks: int = 0, num_ctas: int = 0) -> AttnOptions:
+def _event_handle(e) -> int:
+    """Raw hipEvent_t of a torch.cuda.Event (created on first use) or an int."""
+    if isinstance(e, int):
+        return e
+    if not e.cuda_event:
+        e.record()          # torch creates the underlying event lazily
+    return int(e.cuda_event)
+
+
+def attn_options(chunk_blocks: int = 0, num_ctas: int = 0, kernel_events=None) -> AttnOptions:
     o = AttnOptions()
     o.chunk_blocks = int(chunk_blocks)
     o.num_ctas = int(num_ctas)
+    if kernel_events is not None:
+        e0, e1 = kernel_events
+        o.kernel_events[0] = _event_handle(e0)
+        o.kernel_events[1] = _event_handle(e1)
     return o
 
 
@@ -258,11 +271,13 @@ def stats_bytes(q: torch.Tensor, grid, tile, chunk_blocks: int = 0, num_ctas: in
 
 def sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lists: BlockLists, *,
                 out: Optional[torch.Tensor] = None, stats: Optional[torch.Tensor] = None,
-                chunk_blocks: int = 0, num_ctas: int = 0) -> torch.Tensor:
+                chunk_blocks: int = 0, num_ctas: int = 0, kernel_events=None) -> torch.Tensor:
     """Block-sparse attention over the kept blocks (fva_sparse_attn).
 
     ``stats``: optional uint8 device tensor of ``stats_bytes(...)`` bytes that
     receives the plan header and per-workgroup timing records.
+    ``kernel_events``: optional pair of timing-enabled torch.cuda.Event (or raw
+    hipEvent_t ints) recorded right before and after the attention kernel.
     """
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_device_tensor(name, t)
@@ -276,7 +291,7 @@ def sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lists: BlockL
         out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
     if out.stride() != q.stride() or out.dtype != q.dtype:
         raise ValueError("out must match q's strides and dtype")
-    opts = attn_options(chunk_blocks, num_ctas)
+    opts = attn_options(chunk_blocks, num_ctas, kernel_events)
     wsb = lib.fva_attn_workspace_bytes(ctypes.byref(prob), ctypes.byref(opts))
     if wsb == 0:
         raise FvaError(FVA_ERR_INVALID_ARG, "fva_attn_workspace_bytes")

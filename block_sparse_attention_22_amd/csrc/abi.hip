@@ -103,8 +103,9 @@ struct AttnPlanSizes {
 fva_status attn_sizes(const Geo &g, const fva_attn_options *opts, AttnPlanSizes *s) {
     int chunk = 0, ctas = 0;
     if (opts) {
-        for (int i = 0; i < 6; ++i)
+        for (int i = 0; i < 2; ++i)
             if (opts->reserved[i] != 0) return FVA_ERR_INVALID_ARG;
+        if ((opts->kernel_events[0] == nullptr) != (opts->kernel_events[1] == nullptr)) return FVA_ERR_INVALID_ARG;
         chunk = opts->chunk_blocks;
         ctas = opts->num_ctas;
         if (ctas < 0) return FVA_ERR_INVALID_ARG;
@@ -202,15 +203,13 @@ fva_status fva_route(const fva_problem *prob, const void *q, const void *k, doub
     if (!ws || ws_bytes < L.total || ((uintptr_t)ws % kAlign)) return FVA_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     char *W = static_cast<char *>(ws);
-    int32_t *tok = (int32_t *)(W + L.tok), *bsize = (int32_t *)(W + L.bsize);
     double *qbar = (double *)(W + L.qbar), *kbar = (double *)(W + L.kbar), *SP = (double *)(W + L.sp);
     int32_t *order = (int32_t *)(W + L.order), *base = (int32_t *)(W + L.base), *add = (int32_t *)(W + L.add);
     int32_t *head_base = (int32_t *)(W + L.head_base);
     int32_t *head_kept = out->head_kept ? out->head_kept : (int32_t *)(W + L.head_kept);
     if (!empty) {
-        FVA_TRY_HIP(launch_slot_table(g, tok, bsize, s));
-        FVA_TRY_HIP(launch_pool(g, q, tok, bsize, qbar, s));
-        FVA_TRY_HIP(launch_pool(g, k, tok, bsize, kbar, s));
+        FVA_TRY_HIP(launch_pool(g, q, qbar, s));
+        FVA_TRY_HIP(launch_pool(g, k, kbar, s));
         FVA_TRY_HIP(launch_scores(g, qbar, kbar, SP, s));
         FVA_TRY_HIP(launch_row_select(g, SP, order, base, p, kmin, s));
         FVA_TRY_HIP(launch_augment(g, SP, base, add, head_base, head_kept, budget.mode, budget.frac, s));
@@ -260,9 +259,11 @@ fva_status fva_sparse_attn(const fva_problem *prob, const void *q, const void *k
     const int chunk = opts ? opts->chunk_blocks : 0;
     FVA_TRY_HIP(launch_slot_table(g, tok, bsize, s));
     FVA_TRY_HIP(launch_plan(g, lists->row_ptr, chunk, sz.num_ctas, sz.cap_items, sz.cap_parts, hdr, items, splits, s));
+    hipEvent_t ev0 = opts ? (hipEvent_t)opts->kernel_events[0] : nullptr;
+    hipEvent_t ev1 = opts ? (hipEvent_t)opts->kernel_events[1] : nullptr;
     FVA_TRY_HIP(launch_attention(g, q, k, v, o, lists->col_idx, tok, bsize, hdr, items, part_o, part_ml,
                                  (fva_cta_stat *)stats, (uint16_t *)(W + L.kp), (uint16_t *)(W + L.vt), sz.num_ctas,
-                                 s));
+                                 ev0, ev1, s));
     FVA_TRY_HIP(launch_combine(g, o, tok, bsize, hdr, splits, part_o, part_ml, sz.cap_splits, s));
     return FVA_OK;
 }

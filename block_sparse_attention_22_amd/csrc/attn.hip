@@ -390,24 +390,34 @@ __device__ __forceinline__ int kpos128(int slot, int c) { return c ^ ((slot ^ (s
 // V^T half block: [128 dd][64 slots] bf16, 8-slot group g of row dd at g ^ ((dd >> 1) & 7).
 __device__ __forceinline__ int vpos128(int dd, int g) { return g ^ ((dd >> 1) & 7); }
 
-// Issue the LDS-DMA loads of one half block of packed block j: 4 + 4 wave
-// instructions of 1 KB; each lane fetches the 16-byte chunk that the swizzle
-// places at its LDS position.
-__device__ __forceinline__ void dma_half(uint16_t *Kst, uint16_t *Vst, __amdgpu_buffer_rsrc_t rkp,
-                                         __amdgpu_buffer_rsrc_t rvt, int j, int half, int w, int lane) {
-    const int blk = j * kMaxSlots * 256;              // bytes of one packed block (K or V^T)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int seg = 4 * w + i;                    // 1 KB segment: 4 K rows / 8 V^T rows
-        const int slot = 4 * seg + (lane >> 4);       // K row within the half
-        const int ck = (lane & 15) ^ ((slot ^ (slot >> 3)) & 15);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rkp, (lds_ptr_t)(Kst + seg * 512), 16,
-                                                 blk + (kHalf * half + slot) * 256 + ck * 16, 0, 0, 0);
-        const int dd = 8 * seg + (lane >> 3);
-        const int gv = (lane & 7) ^ ((dd >> 1) & 7);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rvt, (lds_ptr_t)(Vst + seg * 512), 16,
-                                                 blk + dd * 256 + (kHalf * half + 8 * gv) * 2, 0, 0, 0);
+// LDS-DMA of one half block of packed block j: 4 + 4 wave instructions of
+// 1 KB (piece i < 4: K rows, else V^T rows); each lane fetches the 16-byte
+// chunk that the swizzle places at its LDS position.
+struct DmaHalf {
+    uint16_t *Ks, *Vs;
+    __amdgpu_buffer_rsrc_t rkp, rvt;
+    int j, half, w, lane;
+};
+
+__device__ __forceinline__ void dma_piece(const DmaHalf &d, int i) {
+    const int blk = d.j * kMaxSlots * 256;            // bytes of one packed block (K or V^T)
+    const int seg = 4 * d.w + (i & 3);                // 1 KB segment: 4 K rows / 8 V^T rows
+    if (i < 4) {
+        const int slot = 4 * seg + (d.lane >> 4);     // K row within the half
+        const int ck = (d.lane & 15) ^ ((slot ^ (slot >> 3)) & 15);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rkp, (lds_ptr_t)(d.Ks + seg * 512), 16,
+                                                 blk + (kHalf * d.half + slot) * 256 + ck * 16, 0, 0, 0);
+    } else {
+        const int dd = 8 * seg + (d.lane >> 3);
+        const int gv = (d.lane & 7) ^ ((dd >> 1) & 7);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rvt, (lds_ptr_t)(d.Vs + seg * 512), 16,
+                                                 blk + dd * 256 + (kHalf * d.half + 8 * gv) * 2, 0, 0, 0);
     }
+}
+
+__device__ __forceinline__ void dma_half(const DmaHalf &d) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma_piece(d, i);
 }
 
 // Per-lane LDS byte offsets of the MFMA operand reads, fixed for the whole
@@ -437,9 +447,13 @@ __device__ __forceinline__ bf16x8 lds_read16(const uint16_t *base, uint32_t byte
 
 // One 64-key half block for one wave's 32 queries; keys at or past nvalid get
 // zero probability.
+// The DMA of the next half block `dn` is issued one piece per k-step of
+// Q K^T, so the loads are spread over the MFMA stream instead of arriving in
+// one burst; the scheduling groups below keep six operand reads in flight
+// ahead of the MFMAs and put one DMA piece in each group.
 __device__ __forceinline__ void half_tile(const uint16_t *Kt, const uint16_t *Vt, int nvalid, const bf16x8 *qf,
                                           f32x16 *acc, float &m_run, float &l_run, float c, int h,
-                                          const OperandAddr &oa) {
+                                          const OperandAddr &oa, const DmaHalf &dn) {
     f32x16 sacc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -449,17 +463,31 @@ __device__ __forceinline__ void half_tile(const uint16_t *Kt, const uint16_t *Vt
     for (int s = 0; s < 8; ++s) {
         const bf16x8 k0 = lds_read16(Kt, oa.k[s]);
         const bf16x8 k1 = lds_read16(Kt + 32 * 128, oa.k[s ^ 2]);
+        dma_piece(dn, s);
         sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], sacc[0], 0, 0, 0);
         sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], sacc[1], 0, 0, 0);
     }
+    // masks: 0x100 LDS read, 0x020 VMEM read, 0x008 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int s = 0; s < 5; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
     if (nvalid < kHalf) {
+        // key 32t + 16(r/8) + 8h + r%8 is masked when it reaches nvalid
+        const int lim = nvalid - 8 * h;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = 32 * t + 16 * (r >> 3) + 8 * h + (r & 7);
-                if (key >= nvalid) sacc[t][r] = -INFINITY;
-            }
+            for (int r = 0; r < 16; ++r)
+                if (32 * t + 16 * (r >> 3) + (r & 7) >= lim) sacc[t][r] = -INFINITY;
     }
     float mloc = -INFINITY;
 #pragma unroll
@@ -561,7 +589,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
             int j1 = (nkb > 1) ? cols[1] : 0;
             int n1 = (nkb > 1) ? bsz[j1] : 0;
             int j2 = (nkb > 2) ? cols[2] : 0;
-            dma_half(Ks0, Vs0, rkp, rvt, j, 0, w, lane);
+            dma_half(DmaHalf{Ks0, Vs0, rkp, rvt, j, 0, w, lane});
             // One step of the stream: wait for the current stage, start the
             // DMA of the next half into the other stage, compute the current.
             // Unrolled by two so both stages are fixed objects in each step.
@@ -572,8 +600,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
                 const int jnext = same ? j : j1;
                 __builtin_amdgcn_s_waitcnt(0x0f70);       // vmcnt(0): this wave's DMA for the current half landed
                 __syncthreads();                          // ... and every wave's; the other stage is free again
-                if (jn < nkb) dma_half(Kn, Vn, rkp, rvt, jnext, hn, w, lane);
-                if (active) half_tile(Kc, Vc, nj - hh * kHalf, qf, acc, m_run, l_run, c, h, oa);
+                // After the last half there is nothing to fetch: the DMA then
+                // reloads the current half into the free stage (harmless, and
+                // it keeps the k-step loop free of branches).
+                const bool more = jn < nkb;
+                const DmaHalf dn{Kn, Vn, rkp, rvt, more ? jnext : j, more ? hn : hh, w, lane};
+                if (active) half_tile(Kc, Vc, nj - hh * kHalf, qf, acc, m_run, l_run, c, h, oa, dn);
+                else dma_half(dn);
                 if (jn >= nkb) return false;
                 if (!same) {
                     jj = jn;
@@ -586,6 +619,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
             };
             while (step(Ks0, Vs0, Ks1, Vs1) && step(Ks1, Vs1, Ks0, Vs0)) {
             }
+            __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): the last (reload) DMA has landed
             __syncthreads();       // all waves done with both stages before the next item's DMA
         }
         const float l = l_run + __shfl_xor(l_run, 32, 64);
@@ -630,39 +664,44 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
 // slots], slots past the block's tokens zero.  Each thread moves 8 slots of one
 // 16-byte chunk and transposes its 8x8 V tile in registers.
 __global__ __launch_bounds__(256) void pack_kv_kernel(Geo g, const uint16_t *K, const uint16_t *V,
-                                                      const int32_t *tok, const int32_t *bsize, uint16_t *Kp,
-                                                      uint16_t *Vt) {
+                                                      uint16_t *Kp, uint16_t *Vt) {
     const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-    const int cv = tid >> 4, g8 = tid & 15;
-    const int n = bsize[j];
+    const BlockTokens bt = block_tokens(g, j);
     const int64_t hoff = (int64_t)(bh / g.H) * g.sb + (int64_t)(bh % g.H) * g.sh;
     const int64_t pblk = ((int64_t)bh * g.Nb + j) * kMaxSlots * 128;
+    const int c16 = tid & 15, hi = tid >> 4;
     // K: 16 lanes move one 256-byte row (coalesced reads and writes).
+    u32x4 kx[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-        const int slot = (tid >> 4) + 16 * m, ck = tid & 15;
-        const int t = tok[j * kMaxSlots + slot];
-        u32x4 kx = *reinterpret_cast<const u32x4 *>(K + hoff + (int64_t)t * g.sn + ck * 8);
-        if (slot >= n) kx = u32x4{0, 0, 0, 0};
-        *reinterpret_cast<u32x4 *>(Kp + pblk + slot * 128 + ck * 8) = kx;
+        const int slot = hi + 16 * m;
+        kx[m] = *reinterpret_cast<const u32x4 *>(K + hoff + (int64_t)bt.token(slot) * g.sn + c16 * 8);
     }
-    // V: 8 slots x one 16-byte chunk per thread, transposed in registers.
+    // V: slots 8*hi .. 8*hi+7 of the 16-byte chunk c16 (16 lanes read one
+    // token row), transposed in registers to 8 dd rows x 8 slots.
     u32x4 in[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        const int slot = 8 * g8 + s;
-        const int t = tok[j * kMaxSlots + slot];
-        in[s] = *reinterpret_cast<const u32x4 *>(V + hoff + (int64_t)t * g.sn + cv * 8);
-        if (slot >= n) in[s] = u32x4{0, 0, 0, 0};
+    for (int s8 = 0; s8 < 8; ++s8) {
+        const int slot = 8 * hi + s8;
+        in[s8] = *reinterpret_cast<const u32x4 *>(V + hoff + (int64_t)bt.token(slot) * g.sn + c16 * 8);
     }
 #pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const int slot = hi + 16 * m;
+        if (slot >= bt.n) kx[m] = u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4 *>(Kp + pblk + slot * 128 + c16 * 8) = kx[m];
+    }
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8)
+        if (8 * hi + s8 >= bt.n) in[s8] = u32x4{0, 0, 0, 0};
+#pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const int dd = 8 * cv + e;
+        const int dd = 8 * c16 + e;
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
         u32x4 o;
 #pragma unroll
         for (int w = 0; w < 4; ++w) o[w] = __builtin_amdgcn_perm(in[2 * w + 1][e >> 1], in[2 * w][e >> 1], sel);
-        *reinterpret_cast<u32x4 *>(Vt + pblk + dd * kMaxSlots + 8 * g8) = o;
+        *reinterpret_cast<u32x4 *>(Vt + pblk + dd * kMaxSlots + 8 * hi) = o;
     }
 }
 
@@ -906,7 +945,8 @@ hipError_t launch_plan(const Geo &g, const int32_t *row_ptr, int chunk_mode, int
 hipError_t launch_attention(const Geo &g, const void *q, const void *k, const void *v, void *o,
                             const int32_t *col_idx, const int32_t *tok, const int32_t *bsize, PlanHeader *hdr,
                             const WorkItem *items, float *part_o, float *part_ml, fva_cta_stat *stats,
-                            uint16_t *kp, uint16_t *vt, int num_ctas, hipStream_t s) {
+                            uint16_t *kp, uint16_t *vt, int num_ctas, hipEvent_t ev0, hipEvent_t ev1,
+                            hipStream_t s) {
     AttnArgs a;
     a.g = g;
     a.q = q; a.k = k; a.v = v; a.o = o;
@@ -915,21 +955,29 @@ hipError_t launch_attention(const Geo &g, const void *q, const void *k, const vo
     a.part_o = part_o; a.part_ml = part_ml;
     a.stats = stats;
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.D));
-    if (g.dtype == FVA_BF16) {
-        if (g.D == 128) {
-            hipLaunchKernelGGL(pack_kv_kernel, dim3(g.Nb, g.BH), dim3(256), 0, s, g, (const uint16_t *)k,
-                               (const uint16_t *)v, tok, bsize, kp, vt);
-            hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-            hipLaunchKernelGGL(attn_bf16_d128_kernel, dim3(num_ctas), dim3(256), 0, s, a, kp, vt);
-        } else {
-            hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(num_ctas), dim3(256), 0, s, a);
-        }
-    } else {
-        if (g.D == 128) hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(num_ctas), dim3(kMaxSlots), 0, s, a);
-        else hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(num_ctas), dim3(kMaxSlots), 0, s, a);
+    const bool d128 = (g.dtype == FVA_BF16 && g.D == 128);
+    if (d128) {
+        hipLaunchKernelGGL(pack_kv_kernel, dim3(g.Nb, g.BH), dim3(256), 0, s, g, (const uint16_t *)k,
+                           (const uint16_t *)v, kp, vt);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    return hipGetLastError();
+    if (ev0) {
+        hipError_t e = hipEventRecord(ev0, s);
+        if (e != hipSuccess) return e;
+    }
+    if (d128)
+        hipLaunchKernelGGL(attn_bf16_d128_kernel, dim3(num_ctas), dim3(256), 0, s, a, kp, vt);
+    else if (g.dtype == FVA_BF16)
+        hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(num_ctas), dim3(256), 0, s, a);
+    else if (g.D == 128)
+        hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(num_ctas), dim3(kMaxSlots), 0, s, a);
+    else
+        hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(num_ctas), dim3(kMaxSlots), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (ev1) e = hipEventRecord(ev1, s);
+    return e;
 }
 
 hipError_t launch_combine(const Geo &g, void *o, const int32_t *tok, const int32_t *bsize, const PlanHeader *hdr,

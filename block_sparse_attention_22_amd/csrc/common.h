@@ -43,11 +43,37 @@ struct PlanHeader {
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Token layout of one block: its first token t0, the extent (et, ey, ex) of
+// the (possibly clipped) tile and the token count n.  Slot r < n is token
+// t0 + (dt*Y + dy)*X + dx with (dt, dy, dx) the raster position of r in the
+// tile; slots at or past n stand for t0.
+struct BlockTokens {
+    int t0, ey, ex, n, Y, X;
+    __device__ inline int token(int r) const {
+        if (r >= n) return t0;
+        const int exy = ey * ex;
+        const int dt = r / exy, rem = r - dt * exy, dy = rem / ex, dx = rem - dy * ex;
+        return t0 + (dt * Y + dy) * X + dx;
+    }
+};
+
+__device__ inline BlockTokens block_tokens(const Geo &g, int j) {
+    const int it = j / (g.nY * g.nX), iy = (j / g.nX) % g.nY, ix = j % g.nX;
+    BlockTokens b;
+    const int et = min(g.tt, g.T - it * g.tt);
+    b.ey = min(g.ty, g.Y - iy * g.ty);
+    b.ex = min(g.tx, g.X - ix * g.tx);
+    b.n = et * b.ey * b.ex;
+    b.Y = g.Y;
+    b.X = g.X;
+    b.t0 = ((it * g.tt) * g.Y + iy * g.ty) * g.X + ix * g.tx;
+    return b;
+}
+
 // ---------------------------------------------------------------- launches
 // Routing (route.hip)
 hipError_t launch_slot_table(const Geo &g, int32_t *tok, int32_t *bsize, hipStream_t s);
-hipError_t launch_pool(const Geo &g, const void *x, const int32_t *tok, const int32_t *bsize,
-                       double *out, hipStream_t s);
+hipError_t launch_pool(const Geo &g, const void *x, double *out, hipStream_t s);
 hipError_t launch_scores(const Geo &g, const double *qbar, const double *kbar, double *S, hipStream_t s);
 hipError_t launch_row_select(const Geo &g, double *SP, int32_t *order, int32_t *base, double p,
                              int kmin, hipStream_t s);
@@ -64,7 +90,8 @@ hipError_t launch_plan(const Geo &g, const int32_t *row_ptr, int chunk_mode, int
 hipError_t launch_attention(const Geo &g, const void *q, const void *k, const void *v, void *o,
                             const int32_t *col_idx, const int32_t *tok, const int32_t *bsize,
                             PlanHeader *hdr, const WorkItem *items, float *part_o, float *part_ml,
-                            fva_cta_stat *stats, uint16_t *kp, uint16_t *vt, int num_ctas, hipStream_t s);
+                            fva_cta_stat *stats, uint16_t *kp, uint16_t *vt, int num_ctas, hipEvent_t ev0,
+                            hipEvent_t ev1, hipStream_t s);
 size_t packed_kv_bytes(const Geo &g);
 hipError_t launch_combine(const Geo &g, void *o, const int32_t *tok, const int32_t *bsize,
                           const PlanHeader *hdr, const SplitRow *splits, const float *part_o,

@@ -4,11 +4,10 @@
 // Slack-Aware Sparse Augmentation).
 //
 // Kernels, in launch order:
-//   slot_table   block -> its tokens in tile-local raster order (index math)
 //   pool         mean of Q / K over each block's tokens, float64
 //   scores       s_ij = qbar_i . kbar_j / sqrt(d), float64 tiled GEMM
-//   row_select   per query block: softmax, sort by (mass desc, index asc),
-//                prefix sums, Top-p cut, Top-k floor
+//   row_select   one wave per query block: softmax, register bitonic sort by
+//                (mass desc, index asc), prefix sums, Top-p cut, Top-k floor
 //   head_total / augment
 //                per head: budget, then the not-yet-kept blocks with the
 //                largest mass (ties to lower (i, j)) found by a radix search
@@ -25,8 +24,6 @@
 namespace fva {
 
 namespace {
-
-constexpr int kSortMax = 2048;   // key blocks a row may have
 
 __device__ inline double bits_to_double(uint64_t b) { return __longlong_as_double((long long)b); }
 __device__ inline uint64_t double_bits(double x) { return (uint64_t)__double_as_longlong(x); }
@@ -85,6 +82,7 @@ __device__ inline T block_exclusive_scan(T x, T *tmp, T *total) {
 }
 
 // ------------------------------------------------------------ slot table
+// Used by the attention call (query loads and output stores).
 // tok[b*128 + r] = token index of slot r of block b.  Slots enumerate the
 // tile's existing tokens in (t, y, x) raster order, so an edge tile's tokens
 // are packed at the front; slots at or past bsize[b] repeat the block's first
@@ -121,20 +119,20 @@ __device__ inline void load8(const float *p, float *f) {
 }
 
 // One workgroup per (block, batch*head); out[(bh*Nb + b)*D + c] = mean.
+// Token indices come from the block geometry, so every load is independent.
 template <typename T>
-__global__ __launch_bounds__(256) void pool_kernel(Geo g, const T *x, const int32_t *tok,
-                                                   const int32_t *bsize, double *out) {
+__global__ __launch_bounds__(256) void pool_kernel(Geo g, const T *x, double *out) {
     __shared__ double red[256 * 8];
     const int b = blockIdx.x, bh = blockIdx.y;
     const int CH = g.D / 8, G = 256 / CH;
     const int c = threadIdx.x % CH, grp = threadIdx.x / CH;
     const T *base = x + (int64_t)(bh / g.H) * g.sb + (int64_t)(bh % g.H) * g.sh + c * 8;
-    const int n = bsize[b];
+    const BlockTokens bt = block_tokens(g, b);
+    const int n = bt.n;
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int r = grp; r < n; r += G) {
-        const int t = tok[b * kMaxSlots + r];
         float f[8];
-        load8(base + (int64_t)t * g.sn, f);
+        load8(base + (int64_t)bt.token(r) * g.sn, f);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] += (double)f[e];
     }
@@ -200,84 +198,121 @@ __global__ __launch_bounds__(256) void scores_kernel(Geo g, const double *qbar, 
 }
 
 // ------------------------------------------------------------ row_select
-// One workgroup per (query block, batch*head).  Reads the score row, writes
-// the row's masses sorted descending (in place), the matching key-block
-// order, and the Top-p + floor count.
+// One wave per (query block, batch*head) row, four rows per workgroup.  The
+// row (padded to a power of two NKP = 64*E, padding mass -1 so it sorts last)
+// lives in registers, E entries per lane, entry e = lane*E + r.  A bitonic
+// network orders it by (mass desc, index asc): strides below E exchange
+// registers inside a lane, larger strides exchange with lane ^ (stride/E).
+// Writes the sorted masses (in place), the matching key-block order and the
+// Top-p + floor count.
 __device__ inline bool before(double pa, int ia, double pb, int ib) {
     return pa > pb || (pa == pb && ia < ib);
 }
 
-__global__ __launch_bounds__(256) void row_select_kernel(Geo g, double *SP, int32_t *order,
-                                                         int32_t *base, double p, int kmin, int NKP) {
-    __shared__ double val[kSortMax];
-    __shared__ int32_t idx[kSortMax];
-    __shared__ double dred[256];
-    __shared__ int ired[4];
-    const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+constexpr int kRowsPerGroup = 4;
+
+template <int E>
+__global__ __launch_bounds__(64 * kRowsPerGroup) void row_select_kernel(Geo g, double *SP, int32_t *order,
+                                                                        int32_t *base, double p, int kmin) {
+    constexpr int NKP = 64 * E;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerGroup + (threadIdx.x >> 6);
+    if (row >= (int64_t)g.BH * g.Nb) return;
     const int Nk = g.Nb;
-    const int64_t rowoff = ((int64_t)bh * g.Nb + i) * Nk;
+    double *srow = SP + row * Nk;
+    const int e0 = lane * E;
 
+    double v[E];
+    int id[E];
     double mx = -INFINITY;
-    for (int j = tid; j < Nk; j += 256) {
-        const double s = SP[rowoff + j];
-        val[j] = s;
-        mx = fmax(mx, s);
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+        v[r] = (e0 + r < Nk) ? srow[e0 + r] : -INFINITY;
+        id[r] = e0 + r;
+        mx = fmax(mx, v[r]);
     }
-    mx = block_reduce<256>(mx, dred, [](double a, double b) { return fmax(a, b); });
+    mx = wave_max(mx);
     double sum = 0.0;
-    for (int j = tid; j < Nk; j += 256) {
-        const double e = exp(val[j] - mx);
-        val[j] = e;
-        sum += e;
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+        const double ex = (e0 + r < Nk) ? exp(v[r] - mx) : 0.0;
+        v[r] = ex;
+        sum += ex;
     }
-    sum = block_reduce<256>(sum, dred, [](double a, double b) { return a + b; });
-    for (int j = tid; j < NKP; j += 256) {
-        val[j] = (j < Nk) ? val[j] / sum : -1.0;   // padding sorts last
-        idx[j] = j;
-    }
-    __syncthreads();
+    sum = wave_sum(sum);
+#pragma unroll
+    for (int r = 0; r < E; ++r) v[r] = (e0 + r < Nk) ? v[r] / sum : -1.0;
 
-    // Bitonic sort: final order is "before" (mass desc, index asc).
-    for (int kk = 2; kk <= NKP; kk <<= 1) {
-        for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-            for (int a = tid; a < NKP; a += 256) {
-                const int b = a ^ jj;
-                if (b > a) {
-                    const double va = val[a], vb = val[b];
-                    const int ia = idx[a], ib = idx[b];
-                    const bool up = (a & kk) == 0;
-                    const bool sw = up ? before(vb, ib, va, ia) : before(va, ia, vb, ib);
+    for (int k = 2; k <= NKP; k <<= 1) {
+        for (int j = k >> 1; j >= E; j >>= 1) {
+            const int lm = j / E;
+            const bool lower = (lane & lm) == 0;
+#pragma unroll
+            for (int r = 0; r < E; ++r) {
+                const bool up = ((e0 + r) & k) == 0;
+                const double ov = __shfl_xor(v[r], lm, 64);
+                const int oi = __shfl_xor(id[r], lm, 64);
+                const bool other_first = before(ov, oi, v[r], id[r]);
+                if ((lower == up) ? other_first : !other_first) {
+                    v[r] = ov;
+                    id[r] = oi;
+                }
+            }
+        }
+#pragma unroll
+        for (int j = E / 2; j >= 1; j >>= 1) {
+            if (j < k) {
+#pragma unroll
+                for (int r = 0; r < E; ++r) {
+                    if (r & j) continue;
+                    const bool up = ((e0 + r) & k) == 0;
+                    const bool sw = up ? before(v[r + j], id[r + j], v[r], id[r])
+                                       : before(v[r], id[r], v[r + j], id[r + j]);
                     if (sw) {
-                        val[a] = vb; val[b] = va;
-                        idx[a] = ib; idx[b] = ia;
+                        const double tv = v[r];
+                        v[r] = v[r + j];
+                        v[r + j] = tv;
+                        const int ti = id[r];
+                        id[r] = id[r + j];
+                        id[r + j] = ti;
                     }
                 }
             }
-            __syncthreads();
         }
     }
 
-    // Inclusive prefix sums over contiguous per-thread segments.
-    const int seg = (Nk + 255) / 256;
-    const int s0 = min(Nk, tid * seg), s1 = min(Nk, s0 + seg);
+    // Inclusive prefix sums in sorted order: lane totals, then a wave scan.
     double local = 0.0;
-    for (int j = s0; j < s1; ++j) local += val[j];
-    double total;
-    double run = block_exclusive_scan<256>(local, dred, &total);
-    int first = Nk;
-    for (int j = s0; j < s1; ++j) {
-        run += val[j];
-        if (run >= p) { first = j + 1; break; }
+#pragma unroll
+    for (int r = 0; r < E; ++r) local += (e0 + r < Nk) ? v[r] : 0.0;
+    double incl = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
     }
-    first = block_reduce<256>(first, ired, [](int a, int b) { return min(a, b); });
-    int m_p = (p >= 1.0) ? Nk : first;
+    double run = incl - local;
+    int first = Nk;
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+        if (e0 + r < Nk) {
+            run += v[r];
+            if (run >= p && first == Nk) first = e0 + r + 1;
+        }
+    }
+    first = wave_min(first);
+    const int m_p = (p >= 1.0) ? Nk : first;
     const int m = min(Nk, max(m_p, kmin));
 
-    for (int j = tid; j < Nk; j += 256) {
-        SP[rowoff + j] = val[j];
-        order[rowoff + j] = idx[j];
+    int32_t *orow = order + row * Nk;
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+        if (e0 + r < Nk) {
+            srow[e0 + r] = v[r];
+            orow[e0 + r] = id[r];
+        }
     }
-    if (tid == 0) base[(int64_t)bh * g.Nb + i] = m;
+    if (lane == 0) base[row] = m;
 }
 
 // --------------------------------------------------------------- augment
@@ -473,13 +508,12 @@ hipError_t launch_slot_table(const Geo &g, int32_t *tok, int32_t *bsize, hipStre
     return hipGetLastError();
 }
 
-hipError_t launch_pool(const Geo &g, const void *x, const int32_t *tok, const int32_t *bsize, double *out,
-                       hipStream_t s) {
+hipError_t launch_pool(const Geo &g, const void *x, double *out, hipStream_t s) {
     const dim3 grid(g.Nb, g.BH);
     if (g.dtype == FVA_BF16)
-        hipLaunchKernelGGL(pool_kernel<uint16_t>, grid, dim3(256), 0, s, g, (const uint16_t *)x, tok, bsize, out);
+        hipLaunchKernelGGL(pool_kernel<uint16_t>, grid, dim3(256), 0, s, g, (const uint16_t *)x, out);
     else
-        hipLaunchKernelGGL(pool_kernel<float>, grid, dim3(256), 0, s, g, (const float *)x, tok, bsize, out);
+        hipLaunchKernelGGL(pool_kernel<float>, grid, dim3(256), 0, s, g, (const float *)x, out);
     return hipGetLastError();
 }
 
@@ -491,9 +525,21 @@ hipError_t launch_scores(const Geo &g, const double *qbar, const double *kbar, d
 
 hipError_t launch_row_select(const Geo &g, double *SP, int32_t *order, int32_t *base, double p, int kmin,
                              hipStream_t s) {
-    int nkp = 256;
-    while (nkp < g.Nb) nkp <<= 1;
-    hipLaunchKernelGGL(row_select_kernel, dim3(g.Nb, g.BH), dim3(256), 0, s, g, SP, order, base, p, kmin, nkp);
+    const int64_t R = (int64_t)g.BH * g.Nb;
+    if (R == 0) return hipSuccess;
+    const dim3 grid((unsigned)((R + kRowsPerGroup - 1) / kRowsPerGroup)), block(64 * kRowsPerGroup);
+    if (g.Nb <= 64)
+        hipLaunchKernelGGL(row_select_kernel<1>, grid, block, 0, s, g, SP, order, base, p, kmin);
+    else if (g.Nb <= 128)
+        hipLaunchKernelGGL(row_select_kernel<2>, grid, block, 0, s, g, SP, order, base, p, kmin);
+    else if (g.Nb <= 256)
+        hipLaunchKernelGGL(row_select_kernel<4>, grid, block, 0, s, g, SP, order, base, p, kmin);
+    else if (g.Nb <= 512)
+        hipLaunchKernelGGL(row_select_kernel<8>, grid, block, 0, s, g, SP, order, base, p, kmin);
+    else if (g.Nb <= 1024)
+        hipLaunchKernelGGL(row_select_kernel<16>, grid, block, 0, s, g, SP, order, base, p, kmin);
+    else
+        hipLaunchKernelGGL(row_select_kernel<32>, grid, block, 0, s, g, SP, order, base, p, kmin);
     return hipGetLastError();
 }
 

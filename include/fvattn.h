@@ -115,9 +115,15 @@ typedef struct {
      *  <0 never split (one work item per row);
      *  >0 this chunk size. */
     int32_t chunk_blocks;
-    /* Persistent workgroups; 0 = one per compute unit of the current device. */
+    /* Persistent workgroups; 0 = automatic: as many as fit on the current
+     * device at once (two per compute unit for bf16 d=128, else one). */
     int32_t num_ctas;
-    int32_t reserved[6];  /* must be 0 */
+    int32_t reserved[2];  /* must be 0 */
+    /* Optional caller-owned hipEvent_t pair (both or neither): recorded on
+     * `stream` right before and right after the launch of the attention
+     * kernel proper (after its K/V copies, before the merge of split rows),
+     * so that the caller can time that one kernel. */
+    void *kernel_events[2];
 } fva_attn_options;
 
 /* Written by the device into the optional stats buffer of fva_sparse_attn. */

@@ -75,7 +75,10 @@ def test_attn_workspace_with_explicit_ctas(lib):
     assert lib.fva_attn_workspace_bytes(ctypes.byref(p), ctypes.byref(o)) < ws_auto
     assert lib.fva_attn_stats_bytes(ctypes.byref(p), ctypes.byref(o)) == \
         ctypes.sizeof(fva.PlanInfo) + 256 * ctypes.sizeof(fva.CtaStat)
-    o.reserved[2] = 1
+    o.reserved[1] = 1
+    assert lib.fva_attn_workspace_bytes(ctypes.byref(p), ctypes.byref(o)) == 0
+    o.reserved[1] = 0
+    o.kernel_events[0] = 0x1000        # one event without the other
     assert lib.fva_attn_workspace_bytes(ctypes.byref(p), ctypes.byref(o)) == 0
 
 
@@ -170,3 +173,34 @@ def test_status_strings(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError):
         fva.load_library(str(tmp_path / "missing.so"))
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """Every struct the binding passes has the header's size and field offsets
+    (a C program built with the host compiler prints them)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    structs = {"fva_problem": fva.Problem, "fva_budget": Budget, "fva_lists": ListsC,
+               "fva_attn_options": AttnOptions, "fva_plan_info": fva.PlanInfo, "fva_cta_stat": fva.CtaStat}
+    lines = ['#include <stddef.h>', '#include <stdio.h>', '#include "fvattn.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, *_ in py._fields_:
+            lines.append(f'printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ["return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run([cc, "-std=c99", "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines():
+        a, b, c = line.split()
+        got[(a, b)] = int(c)
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for fname, *_ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
