@@ -34,6 +34,26 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6     # 256 CUs * 2.4 GHz * 4096 bf16 flop/clk/CU, dense
 PEAK_F32_MFMA_TFLOPS = 157.3
 KERNEL_NAME = "attn_bf16_d128_kernel"     # the dominant kernel of the path (bf16, d=128)
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_bf16_d128_kernel_720p_layer_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_attention_22_amd", "csrc", "attn.hip")
+
+
+def measured_traffic():
+    """HBM-side bytes per launch of the attention kernel from the committed
+    FETCH_SIZE/WRITE_SIZE summary (copy-calibrated), or None when the kernel
+    source has changed since the counters were taken."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m_sha = re.search(r"attn\.hip sha256 ([0-9a-f]{64})", text)
+    m_val = re.search(r"traffic_bytes_per_launch attn_bf16_d128_kernel: ([0-9.e+]+)", text)
+    if not (m_sha and m_val) or m_sha.group(1) != src:
+        return None
+    return float(m_val.group(1))
 
 
 def log(*a):
@@ -129,7 +149,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(the path shards by head with no exchange; see the design notes)", file=sys.stderr)
+              "(every step of the path is independent per (batch, head), so more GPUs would each run it on "
+              "their own heads; this benchmark measures the one-GPU share)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -248,7 +269,8 @@ def main():
         "plan": {"n_items": info.n_items, "chunk_blocks": C, "n_split_rows": info.n_split_rows,
                  "n_partials": info.n_partials, "num_ctas": info.num_ctas},
         "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic() if (w.dtype == "bf16" and w.d == 128 and w.cid == 3) else None,
                      "kernel": KERNEL_NAME, "per_launch_flop": flops, "avg_launch_ms": round(kernel_ms, 4)},
     }
     if not args.no_cpu_baseline:

@@ -1,7 +1,8 @@
-// Sparse-routing front end of FVAttn on gfx950 (abstract: Top-p routing, a
-// Top-k safety floor and video-aware block organisation; paperlayer.ai
-// summary, section 3 "FVAttn Design": Sparse-routing frontend and
-// Slack-Aware Sparse Augmentation).
+// Sparse-routing front end of FVAttn on gfx950: blocks that follow the
+// video's 3D layout, a Top-p cut per query block with a minimum block count,
+// and per-head augmentation (FVAttn abstract; paperlayer.ai summary,
+// section 3 "FVAttn Design": Sparse-routing frontend and Slack-Aware Sparse
+// Augmentation).
 //
 // Kernels, in launch order:
 //   pool         mean of Q / K over each block's tokens, float64

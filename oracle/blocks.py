@@ -1,9 +1,9 @@
 """Video-aware block organisation (oracle).
 
 The pages' routing front end groups spatially adjacent tokens into blocks
-before routing (FVAttn abstract: "video-aware block organization"; paperlayer.ai
-summary, section 3 "FVAttn Design", Sparse-routing frontend: nearby tokens in
-nearby blocks).  The reading used here: one block is one 3D tile of
+before routing (FVAttn abstract: blocks organised around the video's layout;
+paperlayer.ai summary, section 3 "FVAttn Design", Sparse-routing frontend:
+nearby tokens in nearby blocks).  The reading used here: one block is one 3D tile of
 (tt, ty, tx) latent tokens, tiles in raster order over the tile grid; an axis
 that is not a multiple of its tile size ends in a partial tile, whose missing
 tokens simply do not exist (they are never keys and produce no output).

@@ -8,16 +8,17 @@ Related Work": Sparse Attention):
 
   O2 pool     mean of Q and of K over each block's tokens;
   O3 scores   block similarity s_ij = qbar_i . kbar_j / sqrt(d) and its row
-              softmax P_ij ("each query block's similarity distribution");
+              softmax P_ij (how each query block's similarity spreads over the
+              key blocks);
   O4 order    per query block, key blocks by P descending, ties to lower j
               (the routing importance order that augmentation follows);
   O5 cut      Top-p: the smallest prefix whose cumulative mass reaches p,
-              then the Top-k safety floor (at least kmin blocks);
+              then a Top-k floor that keeps at least kmin blocks;
   O6 augment  slack-aware augmentation: per head, add the next-highest-mass
               not-yet-kept blocks up to a per-head budget, without changing p;
   O7 csr      per-row kept key blocks, ascending, as CSR.
 
-Readings where the pages are silent (listed again in the design doc):
+Readings where the pages are silent:
   * the score has no block-size correction and uses the same 1/sqrt(d) scale
     as attention;
   * the cut is c_m >= p; p >= 1 (or no prefix reaching p because of
