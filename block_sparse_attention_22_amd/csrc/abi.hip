@@ -214,7 +214,8 @@ fva_status fva_route(const fva_problem *prob, const void *q, const void *k, doub
         FVA_TRY_HIP(launch_row_select(g, SP, order, base, p, kmin, s));
         FVA_TRY_HIP(launch_augment(g, SP, base, add, head_base, head_kept, budget.mode, budget.frac, s));
     }
-    FVA_TRY_HIP(launch_csr(g, order, base, add, out->row_ptr, out->col_idx, out->base_count, out->mask, s));
+    FVA_TRY_HIP(launch_csr(g, order, base, add, head_kept, out->row_ptr, out->col_idx, out->base_count, out->mask,
+                           s));
     return FVA_OK;
 }
 

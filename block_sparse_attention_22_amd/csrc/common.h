@@ -80,8 +80,8 @@ hipError_t launch_row_select(const Geo &g, double *SP, int32_t *order, int32_t *
 hipError_t launch_augment(const Geo &g, const double *SP, const int32_t *base, int32_t *add,
                           int32_t *head_base, int32_t *head_kept, int mode, double frac, hipStream_t s);
 hipError_t launch_csr(const Geo &g, const int32_t *order, const int32_t *base, const int32_t *add,
-                      int32_t *row_ptr, int32_t *col_idx, int32_t *base_out, uint32_t *mask,
-                      hipStream_t s);
+                      const int32_t *head_kept, int32_t *row_ptr, int32_t *col_idx, int32_t *base_out,
+                      uint32_t *mask, hipStream_t s);
 
 // Attention (attn.hip)
 hipError_t launch_plan(const Geo &g, const int32_t *row_ptr, int chunk_mode, int num_ctas,

@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void scores_kernel(Geo g, const double *qbar, 
 // Writes the sorted masses (in place), the matching key-block order and the
 // Top-p + floor count.
 __device__ inline bool before(double pa, int ia, double pb, int ib) {
-    return pa > pb || (pa == pb && ia < ib);
+    return (pa > pb) | ((pa == pb) & (ia < ib));     // bitwise: no short-circuit branch
 }
 
 constexpr int kRowsPerGroup = 4;
@@ -228,7 +228,9 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void row_select_kernel(Geo g, d
     double mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < E; ++r) {
-        v[r] = (e0 + r < Nk) ? srow[e0 + r] : -INFINITY;
+        const bool in = e0 + r < Nk;
+        const double x = srow[min(e0 + r, Nk - 1)];
+        v[r] = in ? x : -INFINITY;
         id[r] = e0 + r;
         mx = fmax(mx, v[r]);
     }
@@ -236,14 +238,16 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void row_select_kernel(Geo g, d
     double sum = 0.0;
 #pragma unroll
     for (int r = 0; r < E; ++r) {
-        const double ex = (e0 + r < Nk) ? exp(v[r] - mx) : 0.0;
+        const double ex = exp(v[r] - mx);    // exp(-inf) = 0 for the padding
         v[r] = ex;
         sum += ex;
     }
     sum = wave_sum(sum);
 #pragma unroll
-    for (int r = 0; r < E; ++r) v[r] = (e0 + r < Nk) ? v[r] / sum : -1.0;
+    for (int r = 0; r < E; ++r) v[r] = (e0 + r < Nk) ? v[r] / sum : -1.0;   // padding sorts last
 
+    // Exchanges are written as selects so that they compile to v_cndmask
+    // rather than divergent branches.
     for (int k = 2; k <= NKP; k <<= 1) {
         for (int j = k >> 1; j >= E; j >>= 1) {
             const int lm = j / E;
@@ -253,11 +257,9 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void row_select_kernel(Geo g, d
                 const bool up = ((e0 + r) & k) == 0;
                 const double ov = __shfl_xor(v[r], lm, 64);
                 const int oi = __shfl_xor(id[r], lm, 64);
-                const bool other_first = before(ov, oi, v[r], id[r]);
-                if ((lower == up) ? other_first : !other_first) {
-                    v[r] = ov;
-                    id[r] = oi;
-                }
+                const bool take = before(ov, oi, v[r], id[r]) != (lower != up);
+                v[r] = take ? ov : v[r];
+                id[r] = take ? oi : id[r];
             }
         }
 #pragma unroll
@@ -267,16 +269,13 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void row_select_kernel(Geo g, d
                 for (int r = 0; r < E; ++r) {
                     if (r & j) continue;
                     const bool up = ((e0 + r) & k) == 0;
-                    const bool sw = up ? before(v[r + j], id[r + j], v[r], id[r])
-                                       : before(v[r], id[r], v[r + j], id[r + j]);
-                    if (sw) {
-                        const double tv = v[r];
-                        v[r] = v[r + j];
-                        v[r + j] = tv;
-                        const int ti = id[r];
-                        id[r] = id[r + j];
-                        id[r + j] = ti;
-                    }
+                    const double va = v[r], vb = v[r + j];
+                    const int ia = id[r], ib = id[r + j];
+                    const bool sw = before(vb, ib, va, ia) == up;
+                    v[r] = sw ? vb : va;
+                    v[r + j] = sw ? va : vb;
+                    id[r] = sw ? ib : ia;
+                    id[r + j] = sw ? ia : ib;
                 }
             }
         }
@@ -290,16 +289,15 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void row_select_kernel(Geo g, d
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         const double y = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += y;
+        incl = (lane >= o) ? incl + y : incl;
     }
     double run = incl - local;
     int first = Nk;
 #pragma unroll
     for (int r = 0; r < E; ++r) {
-        if (e0 + r < Nk) {
-            run += v[r];
-            if (run >= p && first == Nk) first = e0 + r + 1;
-        }
+        const bool in = e0 + r < Nk;
+        run += in ? v[r] : 0.0;
+        first = (in && run >= p && first == Nk) ? e0 + r + 1 : first;
     }
     first = wave_min(first);
     const int m_p = (p >= 1.0) ? Nk : first;
@@ -446,22 +444,34 @@ __global__ __launch_bounds__(kAugThreads) void augment_kernel(Geo g, const doubl
 constexpr int kScanThreads = 1024;
 
 // row_ptr[r] = sum of (base + add) over rows before r; row_ptr[R] = total.
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(int R, const int32_t *base, const int32_t *add,
-                                                            int32_t *row_ptr, int32_t *base_out) {
+// One workgroup per (batch, head): its rows start after the kept blocks of
+// the heads before it (their totals B_h, which augmentation wrote), and are
+// scanned inside the workgroup.  Workgroup BH writes row_ptr[R].
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(Geo g, const int32_t *base, const int32_t *add,
+                                                            const int32_t *head_kept, int32_t *row_ptr,
+                                                            int32_t *base_out) {
     __shared__ int tmp[kScanThreads];
-    const int tid = threadIdx.x;
-    const int seg = (R + kScanThreads - 1) / kScanThreads;
-    const int s0 = min(R, tid * seg), s1 = min(R, s0 + seg);
-    int local = 0;
-    for (int r = s0; r < s1; ++r) local += base[r] + add[r];
-    int total;
-    int run = block_exclusive_scan<kScanThreads>(local, tmp, &total);
-    for (int r = s0; r < s1; ++r) {
-        row_ptr[r] = run;
-        run += base[r] + add[r];
-        if (base_out) base_out[r] = base[r];
+    __shared__ int red[kScanThreads / 64];
+    const int bh = blockIdx.x, tid = threadIdx.x, Nb = g.Nb;
+    int off = 0;
+    for (int h = tid; h < bh; h += kScanThreads) off += head_kept[h];
+    off = block_reduce<kScanThreads>(off, red, [](int a, int b) { return a + b; });
+    if (bh == g.BH) {
+        if (tid == 0) row_ptr[(int64_t)g.BH * Nb] = off;
+        return;
     }
-    if (tid == 0) row_ptr[R] = total;
+    const int64_t r0 = (int64_t)bh * Nb;
+    const int seg = (Nb + kScanThreads - 1) / kScanThreads;
+    const int s0 = min(Nb, tid * seg), s1 = min(Nb, s0 + seg);
+    int local = 0;
+    for (int i = s0; i < s1; ++i) local += base[r0 + i] + add[r0 + i];
+    int total;
+    int run = off + block_exclusive_scan<kScanThreads>(local, tmp, &total);
+    for (int i = s0; i < s1; ++i) {
+        row_ptr[r0 + i] = run;
+        run += base[r0 + i] + add[r0 + i];
+        if (base_out) base_out[r0 + i] = base[r0 + i];
+    }
 }
 
 // One wave per row: bitmask of the first count entries of the row's order,
@@ -555,9 +565,11 @@ hipError_t launch_augment(const Geo &g, const double *SP, const int32_t *base, i
 }
 
 hipError_t launch_csr(const Geo &g, const int32_t *order, const int32_t *base, const int32_t *add,
-                      int32_t *row_ptr, int32_t *col_idx, int32_t *base_out, uint32_t *mask, hipStream_t s) {
+                      const int32_t *head_kept, int32_t *row_ptr, int32_t *col_idx, int32_t *base_out,
+                      uint32_t *mask, hipStream_t s) {
     const int R = g.BH * g.Nb;
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, R, base, add, row_ptr, base_out);
+    hipLaunchKernelGGL(scan_kernel, dim3(g.BH + 1), dim3(kScanThreads), 0, s, g, base, add, head_kept, row_ptr,
+                       base_out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || R == 0) return e;
     hipLaunchKernelGGL(csr_kernel, dim3(g.Nb, g.BH), dim3(64), 0, s, g, order, row_ptr, col_idx, mask);
