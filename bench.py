@@ -14,7 +14,10 @@ fraction of the MI355X dense bf16 MFMA peak (2516.6 TFLOP/s = 256 CUs x
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 
-    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--config 3] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--config 3] [--no-cpu-baseline] [--no-dense]
+
+Besides the step, it times the same attention kernel on dense lists (p = 1,
+every key block kept) once, for the sparse-over-dense attention speedup.
 """
 from __future__ import annotations
 
@@ -143,6 +146,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense (p = 1) comparison")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (HBM counter calibration)")
@@ -273,6 +277,27 @@ def main():
                      "traffic": measured_traffic() if (w.dtype == "bf16" and w.d == 128 and w.cid == 3) else None,
                      "kernel": KERNEL_NAME, "per_launch_flop": flops, "avg_launch_ms": round(kernel_ms, 4)},
     }
+    if not args.no_dense:
+        # Dense comparator: the same kernel on every key block (p = 1), after
+        # the timed region; its lists replace nothing the step uses.
+        log("[bench] dense comparison (p = 1)")
+        dlists = fva.route(qd, kd, 1.0, 0, ("none", 0.0), grid=w.grid, tile=w.tile)
+        dout = torch.empty_like(qd)
+        dev0, dev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fva.sparse_attn(qd, kd, vd, dlists, out=dout, kernel_events=(dev0, dev1))   # warm-up
+        dts = []
+        for _ in range(2):
+            fva.sparse_attn(qd, kd, vd, dlists, out=dout, kernel_events=(dev0, dev1))
+            torch.cuda.synchronize()
+            dts.append(dev0.elapsed_time(dev1))
+        dense_ms = float(np.mean(dts))
+        dense_pairs = int(sizes.sum()) ** 2 * w.B * w.H
+        res["dense"] = {
+            "attn_kernel_ms": round(dense_ms, 3),
+            "tflops": round(4.0 * w.d * dense_pairs / (dense_ms * 1e-3) / 1e12, 2),
+            "sparse_attn_speedup": round(dense_ms / kernel_ms, 3),
+        }
+        del dlists, dout
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle, bounded sample)")
         cb = cpu_baseline(w, q, k, v, rp, ci, budget_s=args.cpu_budget)
