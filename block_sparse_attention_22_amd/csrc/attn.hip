@@ -87,7 +87,33 @@ __device__ inline void write_stats(const AttnArgs &a, uint64_t t0, uint32_t item
 
 // Pull the next work item; every thread of the workgroup gets the same index.
 __device__ inline int next_item(PlanHeader *hdr, int *s_item) {
-    if (threadIdx.x == 0) *s_item = atomicAdd(&hdr->queue, 1);
+    if (threadIdx.x == 0) *s_item = atomicAdd(&hdr->queue[0], 1);
+    __syncthreads();
+    const int it = *s_item;
+    __syncthreads();
+    return it;
+}
+
+// Per-XCD queues: the item list (rows in order) is cut into 8 equal ranges;
+// range q is served first by the workgroups on XCD q, so neighbouring rows,
+// which keep many of the same key blocks, share one L2.  A workgroup whose
+// range is empty moves on to the next range.  cur_q: the range this
+// workgroup is draining (starts at its XCD).
+__device__ inline int next_item_xcd(PlanHeader *hdr, int n_items, int &cur_q, int *s_item) {
+    if (threadIdx.x == 0) {
+        int *qs = hdr->queue;
+        int it = n_items;
+        for (int k = 0; k < 8; ++k) {
+            const int q = cur_q & 7;
+            const int lo = (int)((int64_t)n_items * q / 8), hi = (int)((int64_t)n_items * (q + 1) / 8);
+            if (__hip_atomic_load(&qs[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < hi - lo) {
+                const int t = atomicAdd(&qs[q], 1);
+                if (lo + t < hi) { it = lo + t; break; }
+            }
+            ++cur_q;
+        }
+        *s_item = it;
+    }
     __syncthreads();
     const int it = *s_item;
     __syncthreads();
@@ -374,11 +400,12 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
 // the other wave's matrix work.  Keys are consumed in 64-key half blocks held
 // in a two-stage LDS ring (2 x (16 KB K + 16 KB V^T) per workgroup), filled by
 // LDS-DMA buffer loads issued one half block ahead from the block-major K and
-// V^T copies that pack_kv_kernel writes (so every DMA address is scalar plus
-// lane arithmetic, with no per-lane index loads).  The running row max is only raised when it grows by
-// more than 8 (log2 units), which skips most rescales of the accumulator and
-// keeps probabilities below 2^8 (exact: the same offset is used in numerator
-// and denominator).
+// V^T copies that pack_kv_kernel writes (every DMA address is a per-lane
+// constant plus a wave-uniform block offset, with no per-lane index loads).
+// Work items come from per-XCD queues (next_item_xcd).  The running row max
+// is only raised when it grows by more than 8 (log2 units), which skips most
+// rescales of the accumulator and keeps probabilities below 2^8 (exact: the
+// same offset is used in numerator and denominator).
 constexpr int kHalf = 64;                        // keys per half block
 constexpr int kHalfBytes = kHalf * 128 * 2;      // 16 KB: K or V^T of one half block
 constexpr float kLazyMax = 8.0f;
@@ -393,31 +420,64 @@ __device__ __forceinline__ int vpos128(int dd, int g) { return g ^ ((dd >> 1) & 
 // LDS-DMA of one half block of packed block j: 4 + 4 wave instructions of
 // 1 KB (piece i < 4: K rows, else V^T rows); each lane fetches the 16-byte
 // chunk that the swizzle places at its LDS position.
-struct DmaHalf {
-    uint16_t *Ks, *Vs;
-    __amdgpu_buffer_rsrc_t rkp, rvt;
-    int j, half, w, lane;
+// Per-lane byte offsets of this wave's DMA pieces within one half block of a
+// packed block (K rows: piece i < 4; V^T rows: piece i >= 4); the block and
+// half add a wave-uniform offset.
+struct DmaLane {
+    int off[8];
 };
 
-__device__ __forceinline__ void dma_piece(const DmaHalf &d, int i) {
-    const int blk = d.j * kMaxSlots * 256;            // bytes of one packed block (K or V^T)
-    const int seg = 4 * d.w + (i & 3);                // 1 KB segment: 4 K rows / 8 V^T rows
-    if (i < 4) {
-        const int slot = 4 * seg + (d.lane >> 4);     // K row within the half
-        const int ck = (d.lane & 15) ^ ((slot ^ (slot >> 3)) & 15);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rkp, (lds_ptr_t)(d.Ks + seg * 512), 16,
-                                                 blk + (kHalf * d.half + slot) * 256 + ck * 16, 0, 0, 0);
-    } else {
-        const int dd = 8 * seg + (d.lane >> 3);
-        const int gv = (d.lane & 7) ^ ((dd >> 1) & 7);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rvt, (lds_ptr_t)(d.Vs + seg * 512), 16,
-                                                 blk + dd * 256 + (kHalf * d.half + 8 * gv) * 2, 0, 0, 0);
+__device__ __forceinline__ DmaLane dma_lane(int w, int lane) {
+    DmaLane d;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int seg = 4 * w + i;
+        const int slot = 4 * seg + (lane >> 4);
+        const int ck = (lane & 15) ^ ((slot ^ (slot >> 3)) & 15);
+        d.off[i] = slot * 256 + ck * 16;
+        const int dd = 8 * seg + (lane >> 3);
+        const int gv = (lane & 7) ^ ((dd >> 1) & 7);
+        d.off[4 + i] = dd * 256 + 8 * gv * 2;
     }
+    return d;
 }
 
-__device__ __forceinline__ void dma_half(const DmaHalf &d) {
+// The next half block to fetch: destination stages, packed block j, half.
+struct DmaHalf {
+    uint32_t kst, vst;        // LDS byte addresses of this wave's first 1 KB segment of each stage
+    __amdgpu_buffer_rsrc_t rkp, rvt;
+    int j, half;
+};
+
+// One 1 KB LDS-DMA (16 bytes per lane), issued through inline assembly so
+// that the compiler does not track it: with the builtin, the compiler's own
+// waits for these loads were conservative (all outstanding loads) wherever
+// it could not tell the stages apart.  The kernel waits explicitly (vmcnt(0)
+// and a barrier) before any wave reads a stage, and makes Q resident before
+// the first DMA of an item.  M0 carries the wave-uniform LDS address; nothing
+// else in the kernel keeps a value in M0 (the clobber is declared, and the
+// warning that M0 is reserved is silenced for this statement only).
+__device__ __forceinline__ void dma16(uint32_t m0v, int voff, int soff, __amdgpu_buffer_rsrc_t rsrc) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "m0");
+#pragma clang diagnostic pop
+}
+
+__device__ __forceinline__ void dma_piece(const DmaHalf &d, const DmaLane &dl, int i) {
+    const int blk = d.j * kMaxSlots * 256;            // bytes of one packed block (K or V^T)
+    if (i < 4)
+        dma16(d.kst + i * 1024, dl.off[i], blk + d.half * (kHalf * 256), d.rkp);
+    else
+        dma16(d.vst + (i - 4) * 1024, dl.off[i], blk + d.half * (kHalf * 2), d.rvt);
+}
+
+__device__ __forceinline__ void dma_half(const DmaHalf &d, const DmaLane &dl) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dma_piece(d, i);
+    for (int i = 0; i < 8; ++i) dma_piece(d, dl, i);
 }
 
 // Per-lane LDS byte offsets of the MFMA operand reads, fixed for the whole
@@ -453,7 +513,7 @@ __device__ __forceinline__ bf16x8 lds_read16(const uint16_t *base, uint32_t byte
 // ahead of the MFMAs and put one DMA piece in each group.
 __device__ __forceinline__ void half_tile(const uint16_t *Kt, const uint16_t *Vt, int nvalid, const bf16x8 *qf,
                                           f32x16 *acc, float &m_run, float &l_run, float c, int h,
-                                          const OperandAddr &oa, const DmaHalf &dn) {
+                                          const OperandAddr &oa, const DmaHalf &dn, const DmaLane &dl) {
     f32x16 sacc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -463,7 +523,7 @@ __device__ __forceinline__ void half_tile(const uint16_t *Kt, const uint16_t *Vt
     for (int s = 0; s < 8; ++s) {
         const bf16x8 k0 = lds_read16(Kt, oa.k[s]);
         const bf16x8 k1 = lds_read16(Kt + 32 * 128, oa.k[s ^ 2]);
-        dma_piece(dn, s);
+        dma_piece(dn, dl, s);
         sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], sacc[0], 0, 0, 0);
         sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], sacc[1], 0, 0, 0);
     }
@@ -546,9 +606,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
     const uint16_t *K = static_cast<const uint16_t *>(a.k);
     uint16_t *O = static_cast<uint16_t *>(a.o);
     const OperandAddr oa = operand_addr(lane);
+    int cur_q = (int)(xcc_id_reg() & 7);
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const DmaLane dl = dma_lane(wu, lane);
+    const uint32_t seg0 = (uint32_t)wu * 4096u;   // this wave's 4 KB share of a stage
 
     for (;;) {
-        const int it = __builtin_amdgcn_readfirstlane(next_item(a.hdr, &s_item));
+        const int it = __builtin_amdgcn_readfirstlane(next_item_xcd(a.hdr, n_items, cur_q, &s_item));
         if (it >= n_items) break;
         WorkItem wi;
         {
@@ -568,6 +632,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
             const u32x4 raw = *reinterpret_cast<const u32x4 *>(Q + boff + (int64_t)qtok * g.sn + 16 * s + 8 * h);
             qf[s] = __builtin_bit_cast(bf16x8, raw);
         }
+        // Q is resident before the stream starts, so that no compiler wait
+        // for these loads lands behind the untracked DMA.
+#pragma unroll
+        for (int s = 0; s < 8; ++s) asm volatile("" : "+v"(qf[s]));
         f32x16 acc[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
@@ -589,7 +657,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
             int j1 = (nkb > 1) ? cols[1] : 0;
             int n1 = (nkb > 1) ? bsz[j1] : 0;
             int j2 = (nkb > 2) ? cols[2] : 0;
-            dma_half(DmaHalf{Ks0, Vs0, rkp, rvt, j, 0, w, lane});
+            auto lds_addr = [](const uint16_t *p) { return (uint32_t)(uintptr_t)(const lds_ptr_t)p; };
+            dma_half(DmaHalf{lds_addr(Ks0) + seg0, lds_addr(Vs0) + seg0, rkp, rvt, j, 0}, dl);
             // One step of the stream: wait for the current stage, start the
             // DMA of the next half into the other stage, compute the current.
             // Unrolled by two so both stages are fixed objects in each step.
@@ -604,9 +673,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
                 // reloads the current half into the free stage (harmless, and
                 // it keeps the k-step loop free of branches).
                 const bool more = jn < nkb;
-                const DmaHalf dn{Kn, Vn, rkp, rvt, more ? jnext : j, more ? hn : hh, w, lane};
-                if (active) half_tile(Kc, Vc, nj - hh * kHalf, qf, acc, m_run, l_run, c, h, oa, dn);
-                else dma_half(dn);
+                const DmaHalf dn{lds_addr(Kn) + seg0, lds_addr(Vn) + seg0, rkp, rvt, more ? jnext : j, more ? hn : hh};
+                if (active) half_tile(Kc, Vc, nj - hh * kHalf, qf, acc, m_run, l_run, c, h, oa, dn, dl);
+                else dma_half(dn, dl);
                 if (jn >= nkb) return false;
                 if (!same) {
                     jj = jn;
@@ -876,7 +945,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int R, const int32_t
         hdr->info.total_blocks = total;
         hdr->info.num_ctas = num_ctas;
         hdr->info.reserved = 0;
-        hdr->queue = 0;
+        for (int q = 0; q < 8; ++q) hdr->queue[q] = 0;
     }
 }
 

@@ -34,11 +34,11 @@ struct SplitRow {
     int32_t row, part_begin, n_parts, pad;
 };
 
-// Device-written plan header followed by the work queue counter.
+// Device-written plan header followed by the work queue counters (one
+// general queue, or one per XCD for the bf16 d=128 kernel).
 struct PlanHeader {
     fva_plan_info info;
-    int32_t queue;
-    int32_t pad[7];
+    int32_t queue[8];
 };
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
