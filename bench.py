@@ -2,8 +2,10 @@
 
 One step = the whole path on one synthetic layer: fva_route (pool, block
 scores, Top-p + floor, slack augmentation, CSR) then fva_sparse_attn (plan,
-block-sparse flash attention, combine), back to back on one stream with the
-inputs already resident in HBM.
+block-sparse flash attention, combine), with the inputs already resident in
+HBM.  The list-independent K/V copies (fva_attn_prepare) run on a second
+stream while the routing runs, joined before the attention; the same step
+on one stream is timed too (ms_per_layer_one_stream).
 
 Workload (default): the 720p-shaped DiT self-attention layer - B=1, 40 heads,
 d=128, bf16, 21x45x80 latent tokens in 2x8x8 tiles, p=0.9, floor 8, +10%
@@ -173,7 +175,31 @@ def main():
     lists = fva.route(qd, kd, w.p, w.kmin, w.budget, grid=w.grid, tile=w.tile)
     out = torch.empty_like(qd)
 
-    def step():
+    main = torch.cuda.current_stream(dev)
+    side = torch.cuda.Stream(dev)          # default priority, like the main stream
+
+    def step(ev=None):
+        # K/V copies on the side stream once the last attention has released
+        # the workspace; routing meanwhile on the main stream; join, attend.
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            if ev:
+                ev[5].record()
+            fva.attn_prepare(kd, vd, grid=w.grid, tile=w.tile)
+            if ev:
+                ev[6].record()
+        if ev:
+            ev[0].record()
+        fva.route(qd, kd, w.p, w.kmin, w.budget, grid=w.grid, tile=w.tile, out=lists)
+        if ev:
+            ev[1].record()
+        main.wait_stream(side)
+        fva.sparse_attn(qd, kd, vd, lists, out=out, prepared=True,
+                        kernel_events=(ev[3], ev[4]) if ev else None)
+        if ev:
+            ev[2].record()
+
+    def step_one_stream():
         fva.route(qd, kd, w.p, w.kmin, w.budget, grid=w.grid, tile=w.tile, out=lists)
         fva.sparse_attn(qd, kd, vd, lists, out=out)
 
@@ -189,12 +215,14 @@ def main():
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
+        step_one_stream()
     torch.cuda.synchronize()
 
-    # Per step: events around the routing call and the attention call (on
-    # torch's current stream, where the library launches), plus the pair the
-    # library records right around the attention kernel proper.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # Per step: events around the routing call and the attention call (main
+    # stream, where the library launches), the pair the library records right
+    # around the attention kernel proper, and a pair around the K/V copies on
+    # the side stream.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     for e in ev:                      # create the kernel events before the timed region
         e[3].record()
         e[4].record()
@@ -203,17 +231,21 @@ def main():
     torch.cuda.synchronize()
     start.record()
     for s in range(args.steps):
-        ev[s][0].record()
-        fva.route(qd, kd, w.p, w.kmin, w.budget, grid=w.grid, tile=w.tile, out=lists)
-        ev[s][1].record()
-        fva.sparse_attn(qd, kd, vd, lists, out=out, kernel_events=(ev[s][3], ev[s][4]))
-        ev[s][2].record()
+        step(ev[s])
     stop.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(stop) / args.steps
     route_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     kernel_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in ev]))
+    prepare_ms = float(np.mean([e[5].elapsed_time(e[6]) for e in ev]))
+    # The same step on one stream (everything in order), for comparison.
+    start.record()
+    for s in range(args.steps):
+        step_one_stream()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_one_stream = start.elapsed_time(stop) / args.steps
 
     # Lists, pair count and balance (one more call with per-workgroup stats).
     rp = lists.row_ptr.cpu().numpy().astype(np.int64)
@@ -256,7 +288,9 @@ def main():
         "config": {"workload": w.name, "B": w.B, "heads": w.H, "head_dim": w.d, "grid": list(w.grid),
                    "tile": list(w.tile), "p": w.p, "kmin": w.kmin, "budget": list(w.budget), "tokens": w.N},
         "ms_per_layer": round(ms_step, 4),
+        "ms_per_layer_one_stream": round(ms_one_stream, 4),
         "route_ms": round(route_ms, 4),
+        "attn_prepare_ms_side_stream": round(prepare_ms, 4),
         "attn_ms": round(attn_ms, 4),
         "attn_kernel_ms": round(kernel_ms, 4),
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),

@@ -48,7 +48,10 @@ class ListsC(ctypes.Structure):
 
 class AttnOptions(ctypes.Structure):
     _fields_ = [("chunk_blocks", ctypes.c_int32), ("num_ctas", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 2), ("kernel_events", ctypes.c_void_p * 2)]
+                ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32), ("kernel_events", ctypes.c_void_p * 2)]
+
+
+FVA_ATTN_PREPARED = 1
 
 
 class PlanInfo(ctypes.Structure):
@@ -63,7 +66,8 @@ class CtaStat(ctypes.Structure):
 
 
 EXPORTS = ("fva_num_blocks", "fva_lists_capacity", "fva_route_workspace_bytes", "fva_route",
-           "fva_attn_workspace_bytes", "fva_attn_stats_bytes", "fva_sparse_attn", "fva_status_string")
+           "fva_attn_workspace_bytes", "fva_attn_stats_bytes", "fva_attn_prepare", "fva_sparse_attn",
+           "fva_status_string")
 
 _lib = None
 _lib_lock = threading.Lock()
@@ -103,6 +107,9 @@ def load_library(path: Optional[str] = None):
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                         P(AttnOptions), ctypes.c_void_p]
         lib.fva_sparse_attn.restype = ctypes.c_int
+        lib.fva_attn_prepare.argtypes = [P(Problem), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_size_t, P(AttnOptions), ctypes.c_void_p]
+        lib.fva_attn_prepare.restype = ctypes.c_int
         lib.fva_status_string.argtypes = [ctypes.c_int]
         lib.fva_status_string.restype = ctypes.c_char_p
         if path is None:
@@ -252,10 +259,11 @@ def _event_handle(e) -> int:
     return int(e.cuda_event)
 
 
-def attn_options(chunk_blocks: int = 0, num_ctas: int = 0, kernel_events=None) -> AttnOptions:
+def attn_options(chunk_blocks: int = 0, num_ctas: int = 0, kernel_events=None, prepared: bool = False) -> AttnOptions:
     o = AttnOptions()
     o.chunk_blocks = int(chunk_blocks)
     o.num_ctas = int(num_ctas)
+    o.flags = FVA_ATTN_PREPARED if prepared else 0
     if kernel_events is not None:
         e0, e1 = kernel_events
         o.kernel_events[0] = _event_handle(e0)
@@ -269,29 +277,58 @@ def stats_bytes(q: torch.Tensor, grid, tile, chunk_blocks: int = 0, num_ctas: in
     return load_library().fva_attn_stats_bytes(ctypes.byref(prob), ctypes.byref(opts))
 
 
-def sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lists: BlockLists, *,
-                out: Optional[torch.Tensor] = None, stats: Optional[torch.Tensor] = None,
-                chunk_blocks: int = 0, num_ctas: int = 0, kernel_events=None) -> torch.Tensor:
-    """Block-sparse attention over the kept blocks (fva_sparse_attn).
-
-    ``stats``: optional uint8 device tensor of ``stats_bytes(...)`` bytes that
-    receives the plan header and per-workgroup timing records.
-    ``kernel_events``: optional pair of timing-enabled torch.cuda.Event (or raw
-    hipEvent_t ints) recorded right before and after the attention kernel.
-    """
+def _check_qkv(q, k, v):
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_device_tensor(name, t)
     if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k and v must share shape and dtype")
     if not (q.stride() == k.stride() == v.stride()):
         raise ValueError("q, k and v must share strides")
+
+
+def attn_prepare(k: torch.Tensor, v: torch.Tensor, *, grid, tile, chunk_blocks: int = 0,
+                 num_ctas: int = 0) -> None:
+    """The list-independent part of sparse_attn (fva_attn_prepare) on the
+    current stream, into the attention workspace that the next
+    ``sparse_attn(..., prepared=True)`` on this device uses with the same
+    k, v and options.  The caller orders the two (and this call after any
+    earlier sparse_attn still reading the workspace), e.g. with
+    ``Stream.wait_stream``."""
+    _check_qkv(k, k, v)
+    lib = load_library()
+    prob = make_problem(k, grid, tile)
+    opts = attn_options(chunk_blocks, num_ctas)
+    wsb = lib.fva_attn_workspace_bytes(ctypes.byref(prob), ctypes.byref(opts))
+    if wsb == 0:
+        raise FvaError(FVA_ERR_INVALID_ARG, "fva_attn_workspace_bytes")
+    ws = _workspace(wsb, k.device, "attn")
+    st = lib.fva_attn_prepare(ctypes.byref(prob), k.data_ptr(), v.data_ptr(), ws.data_ptr(), ws.numel(),
+                              ctypes.byref(opts), _stream(k.device))
+    if st != FVA_OK:
+        raise FvaError(st, "fva_attn_prepare")
+
+
+def sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lists: BlockLists, *,
+                out: Optional[torch.Tensor] = None, stats: Optional[torch.Tensor] = None,
+                chunk_blocks: int = 0, num_ctas: int = 0, kernel_events=None,
+                prepared: bool = False) -> torch.Tensor:
+    """Block-sparse attention over the kept blocks (fva_sparse_attn).
+
+    ``stats``: optional uint8 device tensor of ``stats_bytes(...)`` bytes that
+    receives the plan header and per-workgroup timing records.
+    ``kernel_events``: optional pair of timing-enabled torch.cuda.Event (or raw
+    hipEvent_t ints) recorded right before and after the attention kernel.
+    ``prepared``: ``attn_prepare(k, v, ...)`` already ran (ordered before
+    this call) with the same tensors and options.
+    """
+    _check_qkv(q, k, v)
     lib = load_library()
     prob = make_problem(q, lists.grid, lists.tile)
     if out is None:
         out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
     if out.stride() != q.stride() or out.dtype != q.dtype:
         raise ValueError("out must match q's strides and dtype")
-    opts = attn_options(chunk_blocks, num_ctas, kernel_events)
+    opts = attn_options(chunk_blocks, num_ctas, kernel_events, prepared)
     wsb = lib.fva_attn_workspace_bytes(ctypes.byref(prob), ctypes.byref(opts))
     if wsb == 0:
         raise FvaError(FVA_ERR_INVALID_ARG, "fva_attn_workspace_bytes")
@@ -354,4 +391,4 @@ def per_cu_imbalance(ctas, num_cus: int):
 
 
 __all__ = ["route", "sparse_attn", "BlockLists", "make_problem", "num_blocks", "block_sizes", "load_library", "FvaError",
-           "stats_bytes", "parse_stats", "per_cu_imbalance", "lists_from_csr", "EXPORTS", "LIB_PATH"]
+           "stats_bytes", "parse_stats", "attn_prepare", "FVA_ATTN_PREPARED", "per_cu_imbalance", "lists_from_csr", "EXPORTS", "LIB_PATH"]

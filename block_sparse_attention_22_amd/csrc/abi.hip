@@ -73,7 +73,7 @@ int device_cus() {
 
 // ------------------------------------------------------ route workspace
 struct RouteWs {
-    size_t tok, bsize, qbar, kbar, sp, order, base, add, head_base, head_kept, total;
+    size_t qbar, kbar, sp, order, base, add, head_base, head_kept, total;
 };
 
 RouteWs route_layout(const Geo &g) {
@@ -81,8 +81,6 @@ RouteWs route_layout(const Geo &g) {
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
     const size_t R = (size_t)g.BH * g.Nb;
-    w.tok = take((size_t)g.Nb * kMaxSlots * 4);
-    w.bsize = take((size_t)g.Nb * 4);
     w.qbar = take(R * g.D * 8);
     w.kbar = take(R * g.D * 8);
     w.sp = take(R * g.Nb * 8);
@@ -103,8 +101,7 @@ struct AttnPlanSizes {
 fva_status attn_sizes(const Geo &g, const fva_attn_options *opts, AttnPlanSizes *s) {
     int chunk = 0, ctas = 0;
     if (opts) {
-        for (int i = 0; i < 2; ++i)
-            if (opts->reserved[i] != 0) return FVA_ERR_INVALID_ARG;
+        if (opts->reserved != 0 || (opts->flags & ~FVA_ATTN_PREPARED) != 0) return FVA_ERR_INVALID_ARG;
         if ((opts->kernel_events[0] == nullptr) != (opts->kernel_events[1] == nullptr)) return FVA_ERR_INVALID_ARG;
         chunk = opts->chunk_blocks;
         ctas = opts->num_ctas;
@@ -258,6 +255,8 @@ fva_status fva_sparse_attn(const fva_problem *prob, const void *q, const void *k
     SplitRow *splits = (SplitRow *)(W + L.splits);
     float *part_o = (float *)(W + L.part_o), *part_ml = (float *)(W + L.part_ml);
     const int chunk = opts ? opts->chunk_blocks : 0;
+    if (!(opts && (opts->flags & FVA_ATTN_PREPARED)))
+        FVA_TRY_HIP(launch_pack_kv(g, k, v, (uint16_t *)(W + L.kp), (uint16_t *)(W + L.vt), s));
     FVA_TRY_HIP(launch_slot_table(g, tok, bsize, s));
     FVA_TRY_HIP(launch_plan(g, lists->row_ptr, chunk, sz.num_ctas, sz.cap_items, sz.cap_parts, hdr, items, splits, s));
     hipEvent_t ev0 = opts ? (hipEvent_t)opts->kernel_events[0] : nullptr;
@@ -266,6 +265,23 @@ fva_status fva_sparse_attn(const fva_problem *prob, const void *q, const void *k
                                  (fva_cta_stat *)stats, (uint16_t *)(W + L.kp), (uint16_t *)(W + L.vt), sz.num_ctas,
                                  ev0, ev1, s));
     FVA_TRY_HIP(launch_combine(g, o, tok, bsize, hdr, splits, part_o, part_ml, sz.cap_splits, s));
+    return FVA_OK;
+}
+
+fva_status fva_attn_prepare(const fva_problem *prob, const void *k, const void *v, void *ws, size_t ws_bytes,
+                            const fva_attn_options *opts, void *stream) {
+    Geo g;
+    fva_status st = make_geo(prob, &g);
+    if (st != FVA_OK) return st;
+    AttnPlanSizes sz;
+    st = attn_sizes(g, opts, &sz);
+    if (st != FVA_OK) return st;
+    if (g.BH == 0 || !uses_packed_kv(g)) return FVA_OK;
+    if (!aligned16(k) || !aligned16(v)) return FVA_ERR_INVALID_ARG;
+    const AttnWs L = attn_layout(g, sz);
+    if (!ws || ws_bytes < L.total || ((uintptr_t)ws % kAlign)) return FVA_ERR_WORKSPACE;
+    char *W = static_cast<char *>(ws);
+    FVA_TRY_HIP(launch_pack_kv(g, k, v, (uint16_t *)(W + L.kp), (uint16_t *)(W + L.vt), (hipStream_t)stream));
     return FVA_OK;
 }
 

@@ -1011,6 +1011,15 @@ hipError_t launch_plan(const Geo &g, const int32_t *row_ptr, int chunk_mode, int
     return hipGetLastError();
 }
 
+bool uses_packed_kv(const Geo &g) { return g.dtype == FVA_BF16 && g.D == 128; }
+
+hipError_t launch_pack_kv(const Geo &g, const void *k, const void *v, uint16_t *kp, uint16_t *vt, hipStream_t s) {
+    if (!uses_packed_kv(g) || g.BH == 0) return hipSuccess;
+    hipLaunchKernelGGL(pack_kv_kernel, dim3(g.Nb, g.BH), dim3(256), 0, s, g, (const uint16_t *)k,
+                       (const uint16_t *)v, kp, vt);
+    return hipGetLastError();
+}
+
 hipError_t launch_attention(const Geo &g, const void *q, const void *k, const void *v, void *o,
                             const int32_t *col_idx, const int32_t *tok, const int32_t *bsize, PlanHeader *hdr,
                             const WorkItem *items, float *part_o, float *part_ml, fva_cta_stat *stats,
@@ -1024,13 +1033,7 @@ hipError_t launch_attention(const Geo &g, const void *q, const void *k, const vo
     a.part_o = part_o; a.part_ml = part_ml;
     a.stats = stats;
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)g.D));
-    const bool d128 = (g.dtype == FVA_BF16 && g.D == 128);
-    if (d128) {
-        hipLaunchKernelGGL(pack_kv_kernel, dim3(g.Nb, g.BH), dim3(256), 0, s, g, (const uint16_t *)k,
-                           (const uint16_t *)v, kp, vt);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
+    const bool d128 = uses_packed_kv(g);
     if (ev0) {
         hipError_t e = hipEventRecord(ev0, s);
         if (e != hipSuccess) return e;

@@ -93,6 +93,8 @@ hipError_t launch_attention(const Geo &g, const void *q, const void *k, const vo
                             fva_cta_stat *stats, uint16_t *kp, uint16_t *vt, int num_ctas, hipEvent_t ev0,
                             hipEvent_t ev1, hipStream_t s);
 size_t packed_kv_bytes(const Geo &g);
+bool uses_packed_kv(const Geo &g);
+hipError_t launch_pack_kv(const Geo &g, const void *k, const void *v, uint16_t *kp, uint16_t *vt, hipStream_t s);
 hipError_t launch_combine(const Geo &g, void *o, const int32_t *tok, const int32_t *bsize,
                           const PlanHeader *hdr, const SplitRow *splits, const float *part_o,
                           const float *part_ml, int cap_splits, hipStream_t s);

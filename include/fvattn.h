@@ -13,6 +13,8 @@
  *                    (abstract; paperlayer.ai summary, section 3 "FVAttn
  *                    Design": Sparse-routing frontend, Slack-Aware Sparse
  *                    Augmentation);
+ *   fva_attn_prepare the list-independent part of fva_sparse_attn (K/V
+ *                    copies), for overlap with fva_route on another stream
  *   fva_sparse_attn  exact softmax attention over only the kept key blocks
  *                    (section 2 "Background and Related Work": dynamic
  *                    block-sparse attention), with a work-list balancer that
@@ -108,6 +110,8 @@ typedef struct {
     uint32_t *mask;       /* [batch*heads*Nq*ceil(Nk/32)] bit j of row r = block j kept; may be NULL */
 } fva_lists;
 
+#define FVA_ATTN_PREPARED 1
+
 /* Balancer options for fva_sparse_attn; pass NULL for the defaults (all 0). */
 typedef struct {
     /* Split rows into work items of at most this many key blocks:
@@ -118,7 +122,11 @@ typedef struct {
     /* Persistent workgroups; 0 = automatic: as many as fit on the current
      * device at once (two per compute unit for bf16 d=128, else one). */
     int32_t num_ctas;
-    int32_t reserved[2];  /* must be 0 */
+    /* FVA_ATTN_PREPARED: the workspace already holds the K/V copies that
+     * fva_attn_prepare wrote for the same problem, k, v and options, so
+     * fva_sparse_attn skips them.  No other bit may be set. */
+    int32_t flags;
+    int32_t reserved;     /* must be 0 */
     /* Optional caller-owned hipEvent_t pair (both or neither): recorded on
      * `stream` right before and right after the launch of the attention
      * kernel proper (after its K/V copies, before the merge of split rows),
@@ -190,6 +198,25 @@ size_t fva_attn_stats_bytes(const fva_problem *prob, const fva_attn_options *opt
 fva_status fva_sparse_attn(const fva_problem *prob, const void *q, const void *k, const void *v,
                            const fva_lists *lists, void *o, void *ws, size_t ws_bytes, void *stats,
                            const fva_attn_options *opts, void *stream);
+
+/*
+ * The part of fva_sparse_attn that does not depend on the block lists: the
+ * block-major K and V^T copies that the bf16 head_dim-128 kernel streams
+ * from (for other problems there is nothing to do and this returns FVA_OK).
+ * Writing them ahead lets a caller run this on a second stream while
+ * fva_route runs, and synchronise only where the data meet (paperlayer.ai
+ * summary of FVAttn, section 3 "FVAttn Design", Overlap/Opt.: runtime work
+ * is issued asynchronously and waits only on true data dependencies).
+ * Then call fva_sparse_attn with the same prob, k, v, ws and options plus
+ * FVA_ATTN_PREPARED in opts->flags, on a stream ordered after this call.
+ * k, v: device, layout of `prob`.  ws, ws_bytes: the attention workspace
+ * (fva_attn_workspace_bytes(prob, opts) bytes).  opts: as for
+ * fva_sparse_attn (its flags are ignored here).  The copies are only ever
+ * read inside the workspace, so a missing or stale preparation gives wrong
+ * numbers, never an out-of-bounds access.
+ */
+fva_status fva_attn_prepare(const fva_problem *prob, const void *k, const void *v, void *ws, size_t ws_bytes,
+                            const fva_attn_options *opts, void *stream);
 
 /* Static string naming a status code. */
 const char *fva_status_string(fva_status s);

@@ -75,9 +75,15 @@ def test_attn_workspace_with_explicit_ctas(lib):
     assert lib.fva_attn_workspace_bytes(ctypes.byref(p), ctypes.byref(o)) < ws_auto
     assert lib.fva_attn_stats_bytes(ctypes.byref(p), ctypes.byref(o)) == \
         ctypes.sizeof(fva.PlanInfo) + 256 * ctypes.sizeof(fva.CtaStat)
-    o.reserved[1] = 1
+    o.reserved = 1
     assert lib.fva_attn_workspace_bytes(ctypes.byref(p), ctypes.byref(o)) == 0
-    o.reserved[1] = 0
+    o.reserved = 0
+    o.flags = fva.FVA_ATTN_PREPARED     # a valid flag does not change the size
+    assert lib.fva_attn_workspace_bytes(ctypes.byref(p), ctypes.byref(o)) == \
+        lib.fva_attn_workspace_bytes(ctypes.byref(p), ctypes.byref(AttnOptions(-1, 256)))
+    o.flags = 2                         # unknown flag bit
+    assert lib.fva_attn_workspace_bytes(ctypes.byref(p), ctypes.byref(o)) == 0
+    o.flags = 0
     o.kernel_events[0] = 0x1000        # one event without the other
     assert lib.fva_attn_workspace_bytes(ctypes.byref(p), ctypes.byref(o)) == 0
 
@@ -155,8 +161,35 @@ def test_attn_rejects_bad_options(lib):
     assert attn_call(lib, opts=o) == FVA_ERR_INVALID_ARG
     o = AttnOptions()
     o.num_ctas = 8
-    o.reserved[0] = 9
+    o.reserved = 9
     assert attn_call(lib, opts=o) == FVA_ERR_INVALID_ARG
+    o.reserved = 0
+    o.flags = 4
+    assert attn_call(lib, opts=o) == FVA_ERR_INVALID_ARG
+
+
+def prepare_call(lib, p=None, k=Q, v=Q, ws=Q, wsb=0, opts=None):
+    p = p or prob()
+    if opts is None:
+        opts = AttnOptions()
+        opts.num_ctas = 256
+    return lib.fva_attn_prepare(ctypes.byref(p), k, v, ws, wsb, ctypes.byref(opts), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), FVA_ERR_INVALID_ARG), (dict(v=Q + 8), FVA_ERR_INVALID_ARG),
+    (dict(ws=None), FVA_ERR_WORKSPACE), (dict(wsb=4096), FVA_ERR_WORKSPACE),
+    (dict(p=prob(dtype=3)), FVA_ERR_UNSUPPORTED), (dict(p=prob(grid_t=0)), FVA_ERR_INVALID_ARG),
+])
+def test_prepare_rejects_before_launch(lib, kw, code):
+    assert prepare_call(lib, **kw) == code
+
+
+def test_prepare_is_a_noop_without_packed_copies(lib):
+    # float32 and head_dim 64 stream K/V directly: nothing to prepare, no pointer is touched
+    assert prepare_call(lib, p=prob(dtype=1), k=None, v=None, ws=None) == FVA_OK
+    assert prepare_call(lib, p=prob(head_dim=64, stride_n=64), k=None, v=None, ws=None) == FVA_OK
+    assert prepare_call(lib, p=prob(heads=0), k=None, v=None, ws=None) == FVA_OK
 
 
 def test_empty_problem_attention_is_noop(lib):

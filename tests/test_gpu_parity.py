@@ -207,3 +207,29 @@ def test_stats_and_per_cu_imbalance(dev):
     imb, busy = fva.per_cu_imbalance(ctas, ncu)
     print(f"\n[stats] ctas={len(ctas)} distinct CU keys={len(busy)} imbalance={imb:.3f}", flush=True)
     assert imb >= 1.0
+
+
+@pytest.mark.parametrize("cid", [1, 2])
+def test_prepare_on_a_side_stream(dev, cid):
+    """attn_prepare on a second stream, overlapped with route on the main
+    stream and joined before sparse_attn(prepared=True), gives the same bits
+    as sparse_attn doing everything itself (the same kernels run on the same
+    data; only the stream of the K/V copies changes)."""
+    w = WORKLOADS[cid]
+    q, k, v, _ = make_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    lists = fva.route(qd, kd, w.p, w.kmin, w.budget, grid=w.grid, tile=w.tile)
+    ref = fva.sparse_attn(qd, kd, vd, lists)
+    torch.cuda.synchronize()
+    main = torch.cuda.current_stream(dev)
+    side = torch.cuda.Stream(dev)
+    for it in range(3):
+        side.wait_stream(main)              # the last sparse_attn is done with the workspace
+        with torch.cuda.stream(side):
+            fva.attn_prepare(kd, vd, grid=w.grid, tile=w.tile)
+        lists2 = fva.route(qd, kd, w.p, w.kmin, w.budget, grid=w.grid, tile=w.tile)
+        main.wait_stream(side)
+        o = fva.sparse_attn(qd, kd, vd, lists2, prepared=True)
+        torch.cuda.synchronize()
+        assert torch.equal(lists2.row_ptr, lists.row_ptr)
+        assert torch.equal(o, ref), (cid, it, (o.float() - ref.float()).abs().max().item())
