@@ -4,8 +4,11 @@ One step = the whole path on one synthetic layer: fva_route (pool, block
 scores, Top-p + floor, slack augmentation, CSR) then fva_sparse_attn (plan,
 block-sparse flash attention, combine), with the inputs already resident in
 HBM.  The list-independent K/V copies (fva_attn_prepare) run on a second
-stream while the routing runs, joined before the attention; the same step
-on one stream is timed too (ms_per_layer_one_stream).
+stream while the routing runs, joined before the attention.  The step is
+timed eagerly (ms_per_layer, `value`), then captured once in a HIP graph
+and timed as replays (ms_per_layer_graph; graph_replay_bit_exact says
+whether a replay reproduced the eager lists and output bit for bit).  The
+same step on one stream is timed too (ms_per_layer_one_stream).
 
 Workload (default): the 720p-shaped DiT self-attention layer - B=1, 40 heads,
 d=128, bf16, 21x45x80 latent tokens in 2x8x8 tiles, p=0.9, floor 8, +10%
@@ -247,6 +250,38 @@ def main():
     torch.cuda.synchronize()
     ms_one_stream = start.elapsed_time(stop) / args.steps
 
+    # The overlapped step captured once in a HIP graph and replayed: the same
+    # kernels without host launch gaps.
+    step()
+    torch.cuda.synchronize()
+    eager_o, eager_rp = out.clone(), lists.row_ptr.clone()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(main)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            main = torch.cuda.current_stream(dev)
+            step()
+    main = torch.cuda.current_stream(dev)
+    main.wait_stream(cap)
+    torch.cuda.synchronize()
+    out.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    graph_ok = bool(torch.equal(out, eager_o) and torch.equal(lists.row_ptr, eager_rp))
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(args.steps):
+        graph.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_graph = start.elapsed_time(stop) / args.steps
+    log(f"[bench] eager {ms_step:.3f} ms, one stream {ms_one_stream:.3f} ms, graph {ms_graph:.3f} ms "
+        f"(replay {'matches' if graph_ok else 'DIFFERS FROM'} eager)")
+    ms_eager = ms_step
+
     # Lists, pair count and balance (one more call with per-workgroup stats).
     rp = lists.row_ptr.cpu().numpy().astype(np.int64)
     ci = lists.col_idx[: int(rp[-1])].cpu().numpy().astype(np.int64)
@@ -288,6 +323,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "heads": w.H, "head_dim": w.d, "grid": list(w.grid),
                    "tile": list(w.tile), "p": w.p, "kmin": w.kmin, "budget": list(w.budget), "tokens": w.N},
         "ms_per_layer": round(ms_step, 4),
+        "ms_per_layer_graph": round(ms_graph, 4),
+        "graph_replay_bit_exact": graph_ok,
         "ms_per_layer_one_stream": round(ms_one_stream, 4),
         "route_ms": round(route_ms, 4),
         "attn_prepare_ms_side_stream": round(prepare_ms, 4),

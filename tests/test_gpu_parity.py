@@ -233,3 +233,48 @@ def test_prepare_on_a_side_stream(dev, cid):
         torch.cuda.synchronize()
         assert torch.equal(lists2.row_ptr, lists.row_ptr)
         assert torch.equal(o, ref), (cid, it, (o.float() - ref.float()).abs().max().item())
+
+
+def test_graph_capture_replays(dev):
+    """route -> attn_prepare (second stream) -> sparse_attn captured in one
+    HIP graph: every replay, with other eager calls on the same workspaces and
+    host synchronisations in between, reproduces the eager lists and output
+    bit for bit.  The library records no memset or copy, only kernels."""
+    w = WORKLOADS[2]
+    q, k, v, _ = make_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    lists = fva.route(qd, kd, w.p, w.kmin, w.budget, grid=w.grid, tile=w.tile)
+    out = torch.empty_like(qd)
+    fva.sparse_attn(qd, kd, vd, lists, out=out)
+    torch.cuda.synchronize()
+    ref_o, ref_rp = out.clone(), lists.row_ptr.clone()
+    ref_ci = lists.col_idx[: int(ref_rp[-1].item())].clone()
+    # other inputs for the eager calls between replays
+    q2, k2 = qd.flip(2).contiguous(), kd.flip(2).contiguous()
+    side = torch.cuda.Stream(dev)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            main = torch.cuda.current_stream(dev)
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                fva.attn_prepare(kd, vd, grid=w.grid, tile=w.tile)
+            fva.route(qd, kd, w.p, w.kmin, w.budget, grid=w.grid, tile=w.tile, out=lists)
+            main.wait_stream(side)
+            fva.sparse_attn(qd, kd, vd, lists, out=out, prepared=True)
+    torch.cuda.current_stream(dev).wait_stream(cap)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.zero_()
+        lists.row_ptr.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(lists.row_ptr, ref_rp), rep
+        assert torch.equal(lists.col_idx[: ref_ci.numel()], ref_ci), rep
+        assert torch.equal(out, ref_o), (rep, (out.float() - ref_o.float()).abs().max().item())
+        # eager work on the same workspaces between replays
+        l2 = fva.route(q2, k2, w.p, w.kmin, w.budget, grid=w.grid, tile=w.tile)
+        fva.sparse_attn(q2, k2, vd, l2)
+        torch.cuda.synchronize()
