@@ -9,6 +9,8 @@ library (no kernels, headers, helpers or tables); inputs come from the
 It is plain numpy, written for checking by eye rather than speed:
 
 * ``blocks``    - video-aware 3D-tile block organisation;
+* ``hilbert``   - the Hilbert-curve block organisation (tokens in curve
+                  order, cut into consecutive 128-token blocks);
 * ``routing``   - mean-pooled block scores, Top-p cut with a Top-k floor,
                   slack-aware augmentation, CSR lists (all in float64);
 * ``attention`` - exact softmax attention restricted to the kept blocks.
@@ -26,6 +28,7 @@ force, closed forms, library routines and hand-worked fixtures in
 ("parity unpinned": it is this project's own definition, not the pages').
 """
 from .blocks import BlockLayout
+from .hilbert import HilbertLayout
 from . import routing, attention
 
-__all__ = ["BlockLayout", "routing", "attention"]
+__all__ = ["BlockLayout", "HilbertLayout", "routing", "attention"]

@@ -300,3 +300,52 @@ def test_kept_pairs_counts_valid_tokens():
     tot, per_head = attention.kept_pairs(lay, rp, ci, 4)
     assert tot == 16 * 30 + 4 * 4 + 8 * 8 + 2 * (16 + 2)
     assert per_head.tolist() == [tot]
+
+
+# --------------------------------------------------------------- Hilbert order
+# The curve's defining properties, each of which a plausible slip breaks: a
+# bijection onto the cube (a lost bit), unit steps between consecutive points
+# (a missing exchange or Gray step; Morton order fails it), and every aligned
+# sub-cube visited as one contiguous run (a snake order fails it).
+import itertools  # noqa: E402
+
+from oracle.hilbert import HilbertLayout, cube_bits, hilbert_index, hilbert_token_order  # noqa: E402
+
+
+@pytest.mark.parametrize("n,bits", [(2, 1), (2, 3), (3, 1), (3, 2), (3, 3), (3, 4)])
+def test_hilbert_is_a_unit_step_bijection(n, bits):
+    pts = np.array(list(itertools.product(range(1 << bits), repeat=n)))
+    h = hilbert_index(pts, bits)
+    assert np.array_equal(np.sort(h), np.arange(len(pts)))
+    walk = pts[np.argsort(h)]
+    assert np.array_equal(walk[0], np.zeros(n, dtype=walk.dtype))          # starts at the origin
+    assert (np.abs(np.diff(walk, axis=0)).sum(axis=1) == 1).all()          # one axis, one step
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_hilbert_visits_aligned_subcubes_contiguously(bits):
+    pts = np.array(list(itertools.product(range(1 << bits), repeat=3)))
+    walk = pts[np.argsort(hilbert_index(pts, bits))]
+    for k in range(1, bits):
+        runs = walk.reshape(-1, 8 ** k, 3) >> k            # runs of 8^k consecutive points
+        assert (runs == runs[:, :1, :]).all()             # one aligned 2^k cube per run
+
+
+def test_hilbert_order_on_a_non_power_of_two_grid():
+    grid = (3, 5, 6)
+    order = hilbert_token_order(grid)
+    assert np.array_equal(np.sort(order), np.arange(90))
+    # the kept tokens follow the curve of the enclosing 8^3 cube
+    full = np.array(list(itertools.product(range(8), repeat=3)))
+    walk = full[np.argsort(hilbert_index(full, 3))]
+    inside = walk[(walk[:, 0] < 3) & (walk[:, 1] < 5) & (walk[:, 2] < 6)]
+    assert np.array_equal(order, (inside[:, 0] * 5 + inside[:, 1]) * 6 + inside[:, 2])
+
+
+@pytest.mark.parametrize("grid,nb,last", [((4, 8, 8), 2, 128), ((5, 30, 52), 61, 120),
+                                          ((21, 45, 80), 591, 80), ((21, 68, 120), 1339, 96)])
+def test_hilbert_layout_blocks(grid, nb, last):
+    lay = HilbertLayout(grid)
+    assert cube_bits(grid) == max(1, int(np.ceil(np.log2(max(grid)))))
+    assert lay.Nb == nb and lay.sizes[-1] == last and (lay.sizes[:-1] == 128).all()
+    assert np.array_equal(np.sort(np.concatenate(lay.members)), np.arange(lay.N))    # a partition
