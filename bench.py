@@ -90,13 +90,13 @@ def simulate_queue(costs, ncta):
     return max(loads) / mean if mean > 0 else 1.0
 
 
-def cpu_baseline(w, q, k, v, g_row_ptr, g_col_idx, budget_s=12.0):
+def cpu_baseline(w, q, k, v, g_row_ptr, g_col_idx, budget_s=12.0, hilbert=False):
     """Time the CPU oracle (unchanged) on a bounded sample of this workload and
     extrapolate to the whole layer: routing of the first heads, attention of a
     seeded sample of query blocks, each until its time budget is used."""
-    from oracle import BlockLayout, attention, routing
+    from oracle import BlockLayout, HilbertLayout, attention, routing
 
-    lay = BlockLayout(w.grid, w.tile)
+    lay = HilbertLayout(w.grid) if hilbert else BlockLayout(w.grid, w.tile)
 
     try:
         from threadpoolctl import threadpool_info
@@ -153,6 +153,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense (p = 1) comparison")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--blocks", choices=("tiles", "hilbert"), default="tiles",
+                    help="block organisation: the workload's 3D tiles, or 128-token runs of the Hilbert-curve order")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -170,12 +172,15 @@ def main():
     dev = torch.device("cuda:0")
     log(f"[bench] generating {w.name}: B={w.B} H={w.H} d={w.d} grid={w.grid} tile={w.tile}")
     q, k, v, gains = make_inputs(w)
-    sizes = fva.block_sizes(w.grid, w.tile)
+    hilbert = args.blocks == "hilbert"
+    order = fva.hilbert_order(w.grid, dev) if hilbert else None
+    blk = dict(grid=w.grid, order=order) if hilbert else dict(grid=w.grid, tile=w.tile)
+    sizes = fva.block_sizes(w.grid, w.tile, ordered=hilbert)
     nb = len(sizes)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     torch.cuda.synchronize()
 
-    lists = fva.route(qd, kd, w.p, w.kmin, w.budget, grid=w.grid, tile=w.tile)
+    lists = fva.route(qd, kd, w.p, w.kmin, w.budget, **blk)
     out = torch.empty_like(qd)
 
     main = torch.cuda.current_stream(dev)
@@ -188,12 +193,12 @@ def main():
         with torch.cuda.stream(side):
             if ev:
                 ev[5].record()
-            fva.attn_prepare(kd, vd, grid=w.grid, tile=w.tile)
+            fva.attn_prepare(kd, vd, **blk)
             if ev:
                 ev[6].record()
         if ev:
             ev[0].record()
-        fva.route(qd, kd, w.p, w.kmin, w.budget, grid=w.grid, tile=w.tile, out=lists)
+        fva.route(qd, kd, w.p, w.kmin, w.budget, **blk, out=lists)
         if ev:
             ev[1].record()
         main.wait_stream(side)
@@ -203,7 +208,7 @@ def main():
             ev[2].record()
 
     def step_one_stream():
-        fva.route(qd, kd, w.p, w.kmin, w.budget, grid=w.grid, tile=w.tile, out=lists)
+        fva.route(qd, kd, w.p, w.kmin, w.budget, **blk, out=lists)
         fva.sparse_attn(qd, kd, vd, lists, out=out)
 
     if args.copy_calibration_mib > 0:
@@ -289,7 +294,7 @@ def main():
     flops = 4.0 * w.d * pairs
     exe_sizes = ((sizes + 31) // 32) * 32        # work the kernel issues: 32-token sub-tiles
     executed_pairs, _ = kept_pairs(rp, ci, exe_sizes, nb)
-    st = torch.zeros(fva.stats_bytes(qd, w.grid, w.tile), dtype=torch.uint8, device=dev)
+    st = torch.zeros(fva.stats_bytes(qd, w.grid, w.tile, order=order), dtype=torch.uint8, device=dev)
     fva.sparse_attn(qd, kd, vd, lists, out=out, stats=st)
     torch.cuda.synchronize()
     info, ctas = fva.parse_stats(st)
@@ -320,8 +325,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded RFF-plus-noise q/k, N(0,1) v; stands in for Wan2.2 activations)",
-        "config": {"workload": w.name, "B": w.B, "heads": w.H, "head_dim": w.d, "grid": list(w.grid),
-                   "tile": list(w.tile), "p": w.p, "kmin": w.kmin, "budget": list(w.budget), "tokens": w.N},
+        "config": {"workload": w.name + ("-hilbert" if hilbert else ""), "B": w.B, "heads": w.H, "head_dim": w.d,
+                   "grid": list(w.grid), "blocks": "hilbert-128" if hilbert else "tiles",
+                   "tile": None if hilbert else list(w.tile), "p": w.p, "kmin": w.kmin, "budget": list(w.budget), "tokens": w.N},
         "ms_per_layer": round(ms_step, 4),
         "ms_per_layer_graph": round(ms_graph, 4),
         "graph_replay_bit_exact": graph_ok,
@@ -345,14 +351,14 @@ def main():
                  "n_partials": info.n_partials, "num_ctas": info.num_ctas},
         "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic() if (w.dtype == "bf16" and w.d == 128 and w.cid == 3) else None,
+                     "traffic": measured_traffic() if (w.dtype == "bf16" and w.d == 128 and w.cid == 3 and not hilbert) else None,
                      "kernel": KERNEL_NAME, "per_launch_flop": flops, "avg_launch_ms": round(kernel_ms, 4)},
     }
     if not args.no_dense:
         # Dense comparator: the same kernel on every key block (p = 1), after
         # the timed region; its lists replace nothing the step uses.
         log("[bench] dense comparison (p = 1)")
-        dlists = fva.route(qd, kd, 1.0, 0, ("none", 0.0), grid=w.grid, tile=w.tile)
+        dlists = fva.route(qd, kd, 1.0, 0, ("none", 0.0), **blk)
         dout = torch.empty_like(qd)
         dev0, dev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         fva.sparse_attn(qd, kd, vd, dlists, out=dout, kernel_events=(dev0, dev1))   # warm-up
@@ -371,7 +377,7 @@ def main():
         del dlists, dout
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle, bounded sample)")
-        cb = cpu_baseline(w, q, k, v, rp, ci, budget_s=args.cpu_budget)
+        cb = cpu_baseline(w, q, k, v, rp, ci, budget_s=args.cpu_budget, hilbert=hilbert)
         attn_full_s = cb["attn_s"] * pairs / max(cb["attn_pairs"], 1)
         full_s = cb["route_full_s"] + attn_full_s
         res["cpu_baseline"] = {

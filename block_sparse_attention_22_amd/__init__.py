@@ -8,6 +8,9 @@ library has not been built, every call raises - there is no fallback.
     lists = route(q, k, p, kmin, budget, grid=(T, Y, X), tile=(tt, ty, tx))
     o     = sparse_attn(q, k, v, lists)
 
+Blocks are 3D tiles (``tile``) or consecutive 128-token runs of a token order
+(``order=hilbert_order(grid, device)`` for the Hilbert-curve organisation).
+
 q, k, v: CUDA (HIP) tensors [B, H, N, d] (bf16 or float32, d in {64, 128},
 last dim contiguous) with N = T*Y*X tokens in (t, y, x) raster order.
 """
@@ -34,7 +37,8 @@ class Problem(ctypes.Structure):
                 ("grid_t", ctypes.c_int32), ("grid_y", ctypes.c_int32), ("grid_x", ctypes.c_int32),
                 ("tile_t", ctypes.c_int32), ("tile_y", ctypes.c_int32), ("tile_x", ctypes.c_int32),
                 ("dtype", ctypes.c_int32),
-                ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64)]
+                ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64),
+                ("token_order", ctypes.c_void_p)]
 
 
 class Budget(ctypes.Structure):
@@ -65,7 +69,7 @@ class CtaStat(ctypes.Structure):
                 ("blocks", ctypes.c_uint32), ("t_start", ctypes.c_uint64), ("t_end", ctypes.c_uint64)]
 
 
-EXPORTS = ("fva_num_blocks", "fva_lists_capacity", "fva_route_workspace_bytes", "fva_route",
+EXPORTS = ("fva_num_blocks", "fva_hilbert_order", "fva_lists_capacity", "fva_route_workspace_bytes", "fva_route",
            "fva_attn_workspace_bytes", "fva_attn_stats_bytes", "fva_attn_prepare", "fva_sparse_attn",
            "fva_status_string")
 
@@ -91,6 +95,8 @@ def load_library(path: Optional[str] = None):
         lib = ctypes.CDLL(p)
         P = ctypes.POINTER
         lib.fva_num_blocks.argtypes = [P(Problem), P(ctypes.c_int32), P(ctypes.c_int32)]
+        lib.fva_hilbert_order.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P(ctypes.c_int32)]
+        lib.fva_hilbert_order.restype = ctypes.c_int
         lib.fva_num_blocks.restype = ctypes.c_int
         lib.fva_lists_capacity.argtypes = [P(Problem)]
         lib.fva_lists_capacity.restype = ctypes.c_size_t
@@ -124,8 +130,20 @@ def status_string(status: int) -> str:
         return "unknown"
 
 
-def make_problem(x: torch.Tensor, grid, tile) -> Problem:
-    """Problem descriptor for a [B, H, N, d] tensor laid out like x."""
+def _check_order(order, N, device):
+    if order is None:
+        return None
+    if not order.is_cuda or order.dtype != torch.int32 or order.dim() != 1 or order.numel() != N \
+            or not order.is_contiguous():
+        raise ValueError(f"order must be a contiguous int32 device tensor of the grid's {N} tokens")
+    if device is not None and order.device != device:
+        raise ValueError("order must live on the device of the activations")
+    return order.data_ptr()
+
+
+def make_problem(x: torch.Tensor, grid, tile, order: Optional[torch.Tensor] = None) -> Problem:
+    """Problem descriptor for a [B, H, N, d] tensor laid out like x; blocks are
+    tiles, or 128-token runs of ``order`` when it is given."""
     if x.dim() != 4:
         raise ValueError("expected a [B, H, N, d] tensor")
     B, H, N, d = x.shape
@@ -140,13 +158,45 @@ def make_problem(x: torch.Tensor, grid, tile) -> Problem:
         dt = FVA_F32
     else:
         raise ValueError(f"unsupported dtype {x.dtype}")
-    tt, ty, tx = (int(a) for a in tile)
-    return Problem(B, H, d, T, Y, X, tt, ty, tx, dt, x.stride(0), x.stride(1), x.stride(2))
+    tt, ty, tx = (int(a) for a in tile) if tile is not None else (1, 1, 1)
+    if tile is None and order is None:
+        raise ValueError("give tile or order")
+    return Problem(B, H, d, T, Y, X, tt, ty, tx, dt, x.stride(0), x.stride(1), x.stride(2),
+                   _check_order(order, N, x.device))
 
 
-def block_sizes(grid, tile):
-    """Valid tokens of every block (tile raster order): edge tiles hold fewer."""
+_hilbert_cache = {}
+
+
+def hilbert_order(grid, device=None) -> torch.Tensor:
+    """Tokens of a T x Y x X grid in 3D Hilbert-curve order (fva_hilbert_order,
+    computed on the host once per grid and device), as int32 on ``device``."""
     import numpy as np
+    T, Y, X = (int(a) for a in grid)
+    key = (T, Y, X, str(device))
+    t = _hilbert_cache.get(key)
+    if t is None:
+        host = np.empty(T * Y * X, dtype=np.int32)
+        st = load_library().fva_hilbert_order(T, Y, X, host.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+        if st != FVA_OK:
+            raise FvaError(st, "fva_hilbert_order")
+        t = torch.from_numpy(host)
+        if device is not None:
+            t = t.to(device)
+        _hilbert_cache[key] = t
+    return t
+
+
+def block_sizes(grid, tile, ordered: bool = False):
+    """Valid tokens of every block: tile raster order (edge tiles hold fewer),
+    or, ``ordered``, 128-token runs of a token order (the last holds the rest)."""
+    import numpy as np
+    if ordered:
+        N = int(grid[0]) * int(grid[1]) * int(grid[2])
+        nb = -(-N // 128)
+        sz = np.full(nb, 128, dtype=np.int64)
+        sz[-1] = N - 128 * (nb - 1)
+        return sz
     ext = []
     for g, t in zip(grid, tile):
         n = -(-int(g) // int(t))
@@ -156,10 +206,11 @@ def block_sizes(grid, tile):
     return (ext[0][:, None, None] * ext[1][None, :, None] * ext[2][None, None, :]).reshape(-1)
 
 
-def num_blocks(grid, tile, *, B=1, H=1, d=128, dtype=torch.bfloat16) -> int:
+def num_blocks(grid, tile, *, B=1, H=1, d=128, dtype=torch.bfloat16, ordered: bool = False) -> int:
     T, Y, X = grid
-    p = Problem(B, H, d, T, Y, X, *tile, FVA_BF16 if dtype == torch.bfloat16 else FVA_F32, H * T * Y * X * d,
-                T * Y * X * d, d)
+    p = Problem(B, H, d, T, Y, X, *(tile if tile is not None else (1, 1, 1)),
+                FVA_BF16 if dtype == torch.bfloat16 else FVA_F32, H * T * Y * X * d, T * Y * X * d, d,
+                256 if ordered else None)      # any aligned non-null address: only the count is computed
     nq, nk = ctypes.c_int32(), ctypes.c_int32()
     st = load_library().fva_num_blocks(ctypes.byref(p), ctypes.byref(nq), ctypes.byref(nk))
     if st != FVA_OK:
@@ -200,7 +251,8 @@ class BlockLists:
     nq: int
     nk: int
     grid: Tuple[int, int, int]
-    tile: Tuple[int, int, int]
+    tile: Optional[Tuple[int, int, int]]
+    order: Optional[torch.Tensor] = None   # token order of the blocks (device int32), or None for tiles
 
     def as_c(self) -> ListsC:
         return ListsC(self.row_ptr.data_ptr(), self.col_idx.data_ptr(), self.base_count.data_ptr(),
@@ -214,7 +266,8 @@ def _budget(budget) -> Budget:
     return Budget(BUDGET_MODES[mode], float(frac))
 
 
-def route(q: torch.Tensor, k: torch.Tensor, p: float, kmin: int, budget=None, *, grid, tile,
+def route(q: torch.Tensor, k: torch.Tensor, p: float, kmin: int, budget=None, *, grid, tile=None,
+          order: Optional[torch.Tensor] = None,
           want_mask: bool = False, out: Optional[BlockLists] = None) -> BlockLists:
     """Sparse-routing front end (fva_route): per-head CSR block lists."""
     _check_device_tensor("q", q)
@@ -222,7 +275,7 @@ def route(q: torch.Tensor, k: torch.Tensor, p: float, kmin: int, budget=None, *,
     if q.shape != k.shape or q.dtype != k.dtype or q.stride() != k.stride():
         raise ValueError("q and k must share shape, dtype and strides")
     lib = load_library()
-    prob = make_problem(q, grid, tile)
+    prob = make_problem(q, grid, tile, order)
     nb = ctypes.c_int32()
     st = lib.fva_num_blocks(ctypes.byref(prob), ctypes.byref(nb), ctypes.byref(ctypes.c_int32()))
     if st != FVA_OK:
@@ -239,7 +292,7 @@ def route(q: torch.Tensor, k: torch.Tensor, p: float, kmin: int, budget=None, *,
             base_count=torch.empty(max(1, R), dtype=torch.int32, device=dev),
             head_kept=torch.empty(max(1, B * H), dtype=torch.int32, device=dev),
             mask=torch.empty(max(1, R * words), dtype=torch.int32, device=dev) if want_mask else None,
-            nq=nb, nk=nb, grid=tuple(grid), tile=tuple(tile))
+            nq=nb, nk=nb, grid=tuple(grid), tile=tuple(tile) if tile is not None else None, order=order)
     wsb = lib.fva_route_workspace_bytes(ctypes.byref(prob))
     ws = _workspace(wsb, dev, "route")
     lc = out.as_c()
@@ -271,8 +324,9 @@ def attn_options(chunk_blocks: int = 0, num_ctas: int = 0, kernel_events=None, p
     return o
 
 
-def stats_bytes(q: torch.Tensor, grid, tile, chunk_blocks: int = 0, num_ctas: int = 0) -> int:
-    prob = make_problem(q, grid, tile)
+def stats_bytes(q: torch.Tensor, grid, tile=None, chunk_blocks: int = 0, num_ctas: int = 0,
+                order: Optional[torch.Tensor] = None) -> int:
+    prob = make_problem(q, grid, tile, order)
     opts = attn_options(chunk_blocks, num_ctas)
     return load_library().fva_attn_stats_bytes(ctypes.byref(prob), ctypes.byref(opts))
 
@@ -286,8 +340,8 @@ def _check_qkv(q, k, v):
         raise ValueError("q, k and v must share strides")
 
 
-def attn_prepare(k: torch.Tensor, v: torch.Tensor, *, grid, tile, chunk_blocks: int = 0,
-                 num_ctas: int = 0) -> None:
+def attn_prepare(k: torch.Tensor, v: torch.Tensor, *, grid, tile=None, chunk_blocks: int = 0,
+                 num_ctas: int = 0, order: Optional[torch.Tensor] = None) -> None:
     """The list-independent part of sparse_attn (fva_attn_prepare) on the
     current stream, into the attention workspace that the next
     ``sparse_attn(..., prepared=True)`` on this device uses with the same
@@ -296,7 +350,7 @@ def attn_prepare(k: torch.Tensor, v: torch.Tensor, *, grid, tile, chunk_blocks: 
     ``Stream.wait_stream``."""
     _check_qkv(k, k, v)
     lib = load_library()
-    prob = make_problem(k, grid, tile)
+    prob = make_problem(k, grid, tile, order)
     opts = attn_options(chunk_blocks, num_ctas)
     wsb = lib.fva_attn_workspace_bytes(ctypes.byref(prob), ctypes.byref(opts))
     if wsb == 0:
@@ -323,7 +377,7 @@ def sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lists: BlockL
     """
     _check_qkv(q, k, v)
     lib = load_library()
-    prob = make_problem(q, lists.grid, lists.tile)
+    prob = make_problem(q, lists.grid, lists.tile, lists.order)
     if out is None:
         out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
     if out.stride() != q.stride() or out.dtype != q.dtype:
@@ -347,7 +401,7 @@ def sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lists: BlockL
     return out
 
 
-def lists_from_csr(row_ptr, col_idx, *, nq, grid, tile, device) -> BlockLists:
+def lists_from_csr(row_ptr, col_idx, *, nq, grid, tile=None, device, order=None) -> BlockLists:
     """Wrap host CSR arrays (e.g. lists made elsewhere) as device BlockLists."""
     rp = torch.as_tensor(row_ptr, dtype=torch.int32).to(device)
     ci = torch.as_tensor(col_idx, dtype=torch.int32)
@@ -357,7 +411,7 @@ def lists_from_csr(row_ptr, col_idx, *, nq, grid, tile, device) -> BlockLists:
     R = rp.numel() - 1
     return BlockLists(row_ptr=rp, col_idx=ci, base_count=torch.empty(max(R, 1), dtype=torch.int32, device=device),
                       head_kept=torch.empty(1, dtype=torch.int32, device=device), mask=None, nq=nq, nk=nq,
-                      grid=tuple(grid), tile=tuple(tile))
+                      grid=tuple(grid), tile=tuple(tile) if tile is not None else None, order=order)
 
 
 def parse_stats(stats: torch.Tensor):
@@ -391,4 +445,4 @@ def per_cu_imbalance(ctas, num_cus: int):
 
 
 __all__ = ["route", "sparse_attn", "BlockLists", "make_problem", "num_blocks", "block_sizes", "load_library", "FvaError",
-           "stats_bytes", "parse_stats", "attn_prepare", "FVA_ATTN_PREPARED", "per_cu_imbalance", "lists_from_csr", "EXPORTS", "LIB_PATH"]
+           "stats_bytes", "parse_stats", "attn_prepare", "FVA_ATTN_PREPARED", "hilbert_order", "per_cu_imbalance", "lists_from_csr", "EXPORTS", "LIB_PATH"]

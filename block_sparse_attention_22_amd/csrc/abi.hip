@@ -5,7 +5,10 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
+#include <utility>
+#include <vector>
 
 #include "common.h"
 
@@ -24,11 +27,17 @@ fva_status make_geo(const fva_problem *p, Geo *g) {
     if (!p) return FVA_ERR_INVALID_ARG;
     if (p->batch < 0 || p->heads < 0) return FVA_ERR_INVALID_ARG;
     if (p->grid_t < 1 || p->grid_y < 1 || p->grid_x < 1) return FVA_ERR_INVALID_ARG;
-    if (p->tile_t < 1 || p->tile_y < 1 || p->tile_x < 1) return FVA_ERR_INVALID_ARG;
+    const bool ordered = p->token_order != nullptr;
+    if (ordered && ((uintptr_t)p->token_order & 3u)) return FVA_ERR_INVALID_ARG;
+    if (!ordered) {
+        if (p->tile_t < 1 || p->tile_y < 1 || p->tile_x < 1) return FVA_ERR_INVALID_ARG;
+    }
     if (p->dtype != FVA_BF16 && p->dtype != FVA_F32) return FVA_ERR_UNSUPPORTED;
     if (p->head_dim != 64 && p->head_dim != 128) return FVA_ERR_UNSUPPORTED;
-    const int64_t vol = (int64_t)p->tile_t * p->tile_y * p->tile_x;
-    if (vol > kMaxSlots) return FVA_ERR_UNSUPPORTED;
+    if (!ordered) {
+        const int64_t vol = (int64_t)p->tile_t * p->tile_y * p->tile_x;
+        if (vol > kMaxSlots) return FVA_ERR_UNSUPPORTED;
+    }
     const int64_t N = (int64_t)p->grid_t * p->grid_y * p->grid_x;
     if (N >= INT32_MAX) return FVA_ERR_INVALID_ARG;
     if (p->stride_n < p->head_dim || (p->stride_n % 8) || p->stride_h < 0 || (p->stride_h % 8) ||
@@ -36,10 +45,10 @@ fva_status make_geo(const fva_problem *p, Geo *g) {
         return FVA_ERR_INVALID_ARG;
     const int64_t elem = (p->dtype == FVA_BF16) ? 2 : 4;
     if (N * p->stride_n * elem >= INT32_MAX) return FVA_ERR_UNSUPPORTED;   // one head's rows span < 2 GiB
-    const int64_t nT = (p->grid_t + p->tile_t - 1) / p->tile_t;
-    const int64_t nY = (p->grid_y + p->tile_y - 1) / p->tile_y;
-    const int64_t nX = (p->grid_x + p->tile_x - 1) / p->tile_x;
-    const int64_t Nb = nT * nY * nX;
+    const int64_t nT = ordered ? 0 : (p->grid_t + p->tile_t - 1) / p->tile_t;
+    const int64_t nY = ordered ? 0 : (p->grid_y + p->tile_y - 1) / p->tile_y;
+    const int64_t nX = ordered ? 0 : (p->grid_x + p->tile_x - 1) / p->tile_x;
+    const int64_t Nb = ordered ? (N + kMaxSlots - 1) / kMaxSlots : nT * nY * nX;
     if (Nb > kMaxBlocks) return FVA_ERR_UNSUPPORTED;
     const int64_t BH = (int64_t)p->batch * p->heads;
     if (BH * Nb * Nb >= INT32_MAX) return FVA_ERR_INVALID_ARG;
@@ -52,7 +61,39 @@ fva_status make_geo(const fva_problem *p, Geo *g) {
     g->BH = (int)BH;
     g->sb = p->stride_b; g->sh = p->stride_h; g->sn = p->stride_n;
     g->dtype = p->dtype;
+    g->order = p->token_order;
     return FVA_OK;
+}
+
+// Position of point (a0, a1, a2) along the 3D Hilbert curve of a 2^bits cube,
+// after J. Skilling, "Programming the Hilbert curve" (AIP Conf. Proc. 707,
+// 2004): undo the per-level reflections and axis exchanges from the top bit
+// down, Gray-encode the axes into the transposed index, then read its bits
+// plane by plane, axis 0 first.
+uint64_t hilbert_key3(uint32_t a0, uint32_t a1, uint32_t a2, int bits) {
+    uint32_t X[3] = {a0, a1, a2};
+    const uint32_t top = 1u << (bits - 1);
+    for (uint32_t Q = top; Q > 1; Q >>= 1) {
+        const uint32_t low = Q - 1;
+        for (int i = 0; i < 3; ++i) {
+            if (X[i] & Q) {
+                X[0] ^= low;
+            } else {
+                const uint32_t t = (X[0] ^ X[i]) & low;
+                X[0] ^= t;
+                X[i] ^= t;
+            }
+        }
+    }
+    X[1] ^= X[0];
+    X[2] ^= X[1];
+    uint32_t mask = 0;
+    for (uint32_t Q = top; Q > 1; Q >>= 1)
+        if (X[2] & Q) mask ^= Q - 1;
+    uint64_t h = 0;
+    for (int b = bits - 1; b >= 0; --b)
+        for (int i = 0; i < 3; ++i) h = (h << 1) | (((X[i] ^ mask) >> b) & 1u);
+    return h;
 }
 
 // Per-device CU count cache (the library's only global state).
@@ -165,6 +206,24 @@ fva_status fva_num_blocks(const fva_problem *prob, int32_t *nq, int32_t *nk) {
     if (!nq || !nk) return FVA_ERR_INVALID_ARG;
     *nq = g.Nb;
     *nk = g.Nb;
+    return FVA_OK;
+}
+
+fva_status fva_hilbert_order(int32_t grid_t, int32_t grid_y, int32_t grid_x, int32_t *order) {
+    if (!order || grid_t < 1 || grid_y < 1 || grid_x < 1) return FVA_ERR_INVALID_ARG;
+    const int64_t N = (int64_t)grid_t * grid_y * grid_x;
+    if (N >= INT32_MAX) return FVA_ERR_INVALID_ARG;
+    const int side = std::max(grid_t, std::max(grid_y, grid_x));
+    int bits = 1;
+    while ((1 << bits) < side) ++bits;
+    if (bits > 21) return FVA_ERR_INVALID_ARG;       // 3 * bits must fit the 64-bit key
+    std::vector<std::pair<uint64_t, int32_t>> key((size_t)N);
+    int32_t n = 0;
+    for (int32_t t = 0; t < grid_t; ++t)
+        for (int32_t y = 0; y < grid_y; ++y)
+            for (int32_t x = 0; x < grid_x; ++x, ++n) key[n] = {hilbert_key3(t, y, x, bits), n};
+    std::sort(key.begin(), key.end());           // keys are distinct: the curve is a bijection
+    for (int64_t i = 0; i < N; ++i) order[i] = key[i].second;
     return FVA_OK;
 }
 

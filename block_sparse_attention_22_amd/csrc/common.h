@@ -21,6 +21,7 @@ struct Geo {
     int BH;
     int64_t sb, sh, sn;
     int dtype;
+    const int32_t *order;   // token order of the blocks (device), or null for 3D tiles
 };
 
 // One unit of attention work: query-block row `row` (= (b*H + h)*Nb + i),
@@ -43,13 +44,17 @@ struct PlanHeader {
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// Token layout of one block: its first token t0, the extent (et, ey, ex) of
-// the (possibly clipped) tile and the token count n.  Slot r < n is token
-// t0 + (dt*Y + dy)*X + dx with (dt, dy, dx) the raster position of r in the
-// tile; slots at or past n stand for t0.
+// Token layout of one block.  Tile blocks: the first token t0, the extent
+// (et, ey, ex) of the (possibly clipped) tile and the token count n; slot
+// r < n is token t0 + (dt*Y + dy)*X + dx with (dt, dy, dx) the raster position
+// of r in the tile.  Order blocks: slot r < n is ord[r] (clamped into the
+// grid, so a malformed order cannot address outside the tensors).  Slots at
+// or past n stand for the block's first token.
 struct BlockTokens {
-    int t0, ey, ex, n, Y, X;
+    int t0, ey, ex, n, Y, X, N;
+    const int32_t *ord;
     __device__ inline int token(int r) const {
+        if (ord) return min(max(ord[r < n ? r : 0], 0), N - 1);
         if (r >= n) return t0;
         const int exy = ey * ex;
         const int dt = r / exy, rem = r - dt * exy, dy = rem / ex, dx = rem - dy * ex;
@@ -58,14 +63,22 @@ struct BlockTokens {
 };
 
 __device__ inline BlockTokens block_tokens(const Geo &g, int j) {
-    const int it = j / (g.nY * g.nX), iy = (j / g.nX) % g.nY, ix = j % g.nX;
     BlockTokens b;
+    b.Y = g.Y;
+    b.X = g.X;
+    b.N = g.N;
+    if (g.order) {
+        b.ord = g.order + (int64_t)j * kMaxSlots;
+        b.n = min(kMaxSlots, g.N - j * kMaxSlots);
+        b.t0 = 0; b.ey = 1; b.ex = 1;
+        return b;
+    }
+    b.ord = nullptr;
+    const int it = j / (g.nY * g.nX), iy = (j / g.nX) % g.nY, ix = j % g.nX;
     const int et = min(g.tt, g.T - it * g.tt);
     b.ey = min(g.ty, g.Y - iy * g.ty);
     b.ex = min(g.tx, g.X - ix * g.tx);
     b.n = et * b.ey * b.ex;
-    b.Y = g.Y;
-    b.X = g.X;
     b.t0 = ((it * g.tt) * g.Y + iy * g.ty) * g.X + ix * g.tx;
     return b;
 }

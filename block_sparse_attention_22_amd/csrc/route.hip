@@ -84,22 +84,16 @@ __device__ inline T block_exclusive_scan(T x, T *tmp, T *total) {
 
 // ------------------------------------------------------------ slot table
 // Used by the attention call (query loads and output stores).
-// tok[b*128 + r] = token index of slot r of block b.  Slots enumerate the
-// tile's existing tokens in (t, y, x) raster order, so an edge tile's tokens
-// are packed at the front; slots at or past bsize[b] repeat the block's first
-// token so that loads never need a guard (their scores are masked and their
-// values multiplied by zero probability).
+// tok[b*128 + r] = token index of slot r of block b (BlockTokens: a tile's
+// existing tokens in (t, y, x) raster order, or the block's run of the token
+// order); slots at or past bsize[b] repeat the block's first token so that
+// loads never need a guard (their scores are masked and their values
+// multiplied by zero probability).
 __global__ __launch_bounds__(kMaxSlots) void slot_table_kernel(Geo g, int32_t *tok, int32_t *bsize) {
     const int b = blockIdx.x, r = threadIdx.x;
-    const int it = b / (g.nY * g.nX), iy = (b / g.nX) % g.nY, ix = b % g.nX;
-    const int et = min(g.tt, g.T - it * g.tt);
-    const int ey = min(g.ty, g.Y - iy * g.ty);
-    const int ex = min(g.tx, g.X - ix * g.tx);
-    const int n = et * ey * ex;
-    const int rr = (r < n) ? r : 0;
-    const int dt = rr / (ey * ex), rem = rr % (ey * ex), dy = rem / ex, dx = rem % ex;
-    tok[b * kMaxSlots + r] = ((it * g.tt + dt) * g.Y + (iy * g.ty + dy)) * g.X + (ix * g.tx + dx);
-    if (r == 0) bsize[b] = n;
+    const BlockTokens bt = block_tokens(g, b);
+    tok[b * kMaxSlots + r] = bt.token(r);
+    if (r == 0) bsize[b] = bt.n;
 }
 
 // ------------------------------------------------------------------ pool
@@ -120,7 +114,8 @@ __device__ inline void load8(const float *p, float *f) {
 }
 
 // One workgroup per (block, batch*head); out[(bh*Nb + b)*D + c] = mean.
-// Token indices come from the block geometry, so every load is independent.
+// Token indices come from the block geometry (or the token order), so every
+// load is independent.
 template <typename T>
 __global__ __launch_bounds__(256) void pool_kernel(Geo g, const T *x, double *out) {
     __shared__ double red[256 * 8];

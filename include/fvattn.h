@@ -64,12 +64,22 @@ typedef enum { FVA_BF16 = 0, FVA_F32 = 1 } fva_dtype;
  * head_dim contiguous, and the given element strides (identical for q, k, v
  * and o; stride_n >= head_dim, all multiples of 8).
  *
- * Blocks are 3D tiles of tile_t x tile_y x tile_x tokens in raster order over
- * the tile grid: block b = (it*nY + iy)*nX + ix with nT = ceil(grid_t/tile_t),
- * nY = ceil(grid_y/tile_y), nX = ceil(grid_x/tile_x) (the pages' "video-aware
- * block organisation").  A tile on the far edge of an axis that is not a
- * multiple of the tile size holds only the tokens that exist; missing tokens
- * are never keys and produce no output.  Nq = Nk = nT*nY*nX.
+ * Blocks (the video-aware block organisation of the routing front end,
+ * paperlayer.ai summary of FVAttn, section 3 "FVAttn Design", Sparse-routing
+ * frontend), one of:
+ *  - token_order == NULL: 3D tiles of tile_t x tile_y x tile_x tokens in
+ *    raster order over the tile grid: block b = (it*nY + iy)*nX + ix with
+ *    nT = ceil(grid_t/tile_t), nY = ceil(grid_y/tile_y), nX =
+ *    ceil(grid_x/tile_x).  A tile on the far edge of an axis that is not a
+ *    multiple of the tile size holds only the tokens that exist; missing
+ *    tokens are never keys and produce no output.  Nq = Nk = nT*nY*nX.
+ *  - token_order != NULL: device int32 [N], 4-byte aligned, a permutation of
+ *    the token indices (for instance the Hilbert-curve order from
+ *    fva_hilbert_order); block b is entries 128*b .. min(128*b + 128, N) - 1,
+ *    so every block is full except possibly the last.  Nq = Nk = ceil(N/128);
+ *    tile_* are ignored.  Entries are clamped into [0, N): a malformed array
+ *    gives wrong results but never an access outside q, k, v or o.  The
+ *    array must stay unchanged while calls that use it run.
  *
  * Supported: head_dim in {64, 128}; dtype FVA_BF16 or FVA_F32;
  * tile volume tile_t*tile_y*tile_x <= 128; batch*heads*Nq*Nk < 2^31.
@@ -81,6 +91,7 @@ typedef struct {
     int32_t tile_t, tile_y, tile_x;
     int32_t dtype;                 /* fva_dtype */
     int64_t stride_b, stride_h, stride_n;
+    const int32_t *token_order;    /* NULL: tile blocks; else block token order (device) */
 } fva_problem;
 
 /*
@@ -153,6 +164,19 @@ typedef struct {
     uint64_t t_start;      /* constant-rate (100 MHz) device clock at start */
     uint64_t t_end;        /* ... and after its last item */
 } fva_cta_stat;
+
+/*
+ * Host only: the tokens of a grid_t x grid_y x grid_x grid in the order of a
+ * 3D Hilbert curve, for token_order (paperlayer.ai summary of FVAttn,
+ * section 3 "FVAttn Design", Sparse-routing frontend: a Hilbert-curve
+ * reordering keeps tokens that are close in the video in nearby blocks).
+ * The curve is J. Skilling's construction ("Programming the Hilbert curve",
+ * 2004) on the smallest cube of side 2^m that holds the grid, axes (t, y, x),
+ * starting at token 0; points outside the grid are skipped.  order: host
+ * int32 [grid_t*grid_y*grid_x], written in full.  FVA_ERR_INVALID_ARG for a
+ * NULL order, a side < 1, N >= 2^31 or a side above 2^21.
+ */
+fva_status fva_hilbert_order(int32_t grid_t, int32_t grid_y, int32_t grid_x, int32_t *order);
 
 /* Number of query and key blocks of a problem.  Host only; FVA_ERR_* on an
  * invalid or unsupported problem. */

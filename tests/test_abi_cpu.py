@@ -237,3 +237,35 @@ def test_struct_layouts_match_the_header(tmp_path):
         assert got[(cname, "size")] == ctypes.sizeof(py), cname
         for fname, *_ in py._fields_:
             assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
+
+
+@pytest.mark.parametrize("grid", [(1, 1, 1), (2, 2, 2), (3, 5, 6), (4, 8, 8), (5, 30, 52), (21, 45, 80)])
+def test_hilbert_order_matches_the_oracle(lib, grid):
+    """The library's host Hilbert order against the oracle's own construction
+    (two independent implementations of the same published curve)."""
+    import numpy as np
+    from oracle.hilbert import hilbert_token_order
+    N = grid[0] * grid[1] * grid[2]
+    out = np.full(N, -7, dtype=np.int32)
+    assert lib.fva_hilbert_order(*grid, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))) == FVA_OK
+    assert np.array_equal(out.astype(np.int64), hilbert_token_order(grid))
+
+
+def test_hilbert_order_rejects_bad_arguments(lib):
+    buf = (ctypes.c_int32 * 8)()
+    assert lib.fva_hilbert_order(2, 2, 2, None) == FVA_ERR_INVALID_ARG
+    assert lib.fva_hilbert_order(0, 2, 2, buf) == FVA_ERR_INVALID_ARG
+    assert lib.fva_hilbert_order(2, -1, 2, buf) == FVA_ERR_INVALID_ARG
+
+
+def test_token_order_problems(lib):
+    p = prob(tile_t=0, tile_y=0, tile_x=0)        # tiles are ignored with a token order ...
+    assert nblocks(lib, p)[0] == FVA_ERR_INVALID_ARG
+    p.token_order = 1 << 20
+    st, nq, nk = nblocks(lib, p)
+    assert st == FVA_OK and nq == nk == 591        # ceil(75600 / 128)
+    p.token_order = (1 << 20) + 2                 # ... but it must be 4-byte aligned
+    assert nblocks(lib, p)[0] == FVA_ERR_INVALID_ARG
+    assert fva.num_blocks((21, 45, 80), None, ordered=True) == 591
+    sz = fva.block_sizes((21, 45, 80), None, ordered=True)
+    assert len(sz) == 591 and sz.sum() == 75600 and sz[-1] == 80

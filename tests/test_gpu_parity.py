@@ -278,3 +278,34 @@ def test_graph_capture_replays(dev):
         l2 = fva.route(q2, k2, w.p, w.kmin, w.budget, grid=w.grid, tile=w.tile)
         fva.sparse_attn(q2, k2, vd, l2)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("cid", [1, 2, 4])
+def test_hilbert_block_parity(dev, cid):
+    """Hilbert-curve blocks (128-token runs of the curve order from the
+    library's host helper) against the oracle's own Hilbert layout: lists by
+    the list rule, outputs within the dtype's tolerance."""
+    from oracle import HilbertLayout
+    w = WORKLOADS[cid]
+    print(f"\n[parity] config {cid} {w.name} with Hilbert blocks", flush=True)
+    q, k, v, _ = make_inputs(w)
+    lay = HilbertLayout(w.grid)
+    npdt = np.float64 if cid <= 2 else np.float32
+    qn, kn, vn = (to_numpy(t, npdt) for t in (q, k, v))
+    ref = routing.route(qn, kn, lay, w.p, w.kmin, w.budget)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    order = fva.hilbert_order(w.grid, dev)
+    assert np.array_equal(order.cpu().numpy().astype(np.int64), lay.order)
+    lists = fva.route(qd, kd, w.p, w.kmin, w.budget, grid=w.grid, order=order)
+    assert lists.nq == lay.Nb
+    g = gpu_lists_to_host(lists)
+    rep = compare_lists(g, ref, w.p, w.budget, lay, w.B, w.H)
+    print(f"[parity] config {cid} hilbert: lists {rep}", flush=True)
+    assert rep["exact_rows"] + rep["excused_count_rows"] + rep["excused_tie_rows"] >= rep["rows"]
+    o = fva.sparse_attn(qd, kd, vd, lists)
+    torch.cuda.synchronize()
+    rows = _rows_sample(w, lay.Nb, SAMPLE[cid])
+    prec = "fp64" if cid <= 2 else "fp32"
+    err = attention_error(o, qn, kn, vn, lay, g["row_ptr"], g["col_idx"], rows=rows, precision=prec)
+    print(f"[parity] config {cid} hilbert: max|o - oracle| = {err:.3e} (tol {TOL[w.dtype]})", flush=True)
+    assert err <= TOL[w.dtype]
