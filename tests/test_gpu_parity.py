@@ -75,8 +75,10 @@ def _small_case(grid, tile, H, d, dtype, seed, scale=1.0, B=1):
     return q, k, v
 
 
-def _run_and_check(dev, q, k, v, grid, tile, p, kmin, budget, tol, chunk=0, strided=False):
-    lay = BlockLayout(grid, tile)
+def _run_and_check(dev, q, k, v, grid, tile, p, kmin, budget, tol, chunk=0, strided=False, hilbert=False):
+    from oracle import HilbertLayout
+    lay = HilbertLayout(grid) if hilbert else BlockLayout(grid, tile)
+    blk = dict(grid=grid, order=fva.hilbert_order(grid, dev)) if hilbert else dict(grid=grid, tile=tile)
     qn, kn, vn = (to_numpy(t) for t in (q, k, v))
     B, H = q.shape[:2]
     ref = routing.route(qn, kn, lay, p, kmin, budget)
@@ -89,7 +91,7 @@ def _run_and_check(dev, q, k, v, grid, tile, p, kmin, budget, tol, chunk=0, stri
         qd, kd, vd = wide(q), wide(k), wide(v)
     else:
         qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    lists = fva.route(qd, kd, p, kmin, budget, grid=grid, tile=tile)
+    lists = fva.route(qd, kd, p, kmin, budget, **blk)
     g = gpu_lists_to_host(lists)
     compare_lists(g, ref, p, budget, lay, B, H)
     out = wide(torch.zeros_like(q)) if strided else torch.empty_like(qd)
@@ -309,3 +311,22 @@ def test_hilbert_block_parity(dev, cid):
     err = attention_error(o, qn, kn, vn, lay, g["row_ptr"], g["col_idx"], rows=rows, precision=prec)
     print(f"[parity] config {cid} hilbert: max|o - oracle| = {err:.3e} (tol {TOL[w.dtype]})", flush=True)
     assert err <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("grid,p,kmin,budget,dtype,d,B,strided", [
+    ((3, 20, 20), 1.0, 0, ("none", 0.0), "bf16", 128, 1, False),      # dense, last block 48 tokens
+    ((1, 5, 5), 0.9, 4, ("none", 0.0), "bf16", 128, 1, False),        # one block smaller than 128
+    ((3, 16, 24), 0.85, 2, ("match_max", 0.0), "bf16", 128, 2, True),  # batch 2, wide token stride
+    ((3, 16, 24), 0.85, 2, ("frac", 0.3), "fp32", 64, 2, True),
+    ((2, 16, 16), 1e-12, 3, ("none", 0.0), "bf16", 64, 1, False),     # p -> 0+: fixed Top-3
+])
+def test_hilbert_edge_cases(dev, grid, p, kmin, budget, dtype, d, B, strided):
+    q, k, v = _small_case(grid, None, 3, d, dtype, 80, scale=2.0, B=B)
+    g, _, _ = _run_and_check(dev, q, k, v, grid, None, p, kmin, budget, TOL[dtype], strided=strided,
+                             hilbert=True)
+    counts = np.diff(g["row_ptr"])
+    nb = -(-grid[0] * grid[1] * grid[2] // 128)
+    if p >= 1.0:
+        assert np.all(counts == nb)
+    if p < 1e-6:
+        assert np.all(counts == min(nb, max(kmin, 1)))
