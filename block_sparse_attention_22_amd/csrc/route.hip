@@ -143,22 +143,28 @@ __global__ __launch_bounds__(256) void pool_kernel(Geo g, const T *x, double *ou
 }
 
 // ---------------------------------------------------------------- scores
-// 64x64 output tile per workgroup; each thread 4x4 outputs (strided so the
-// LDS reads are conflict-free).  S[bh][i][j] = (qbar_i . kbar_j) / sqrt(D).
+// 64x64 output tile per workgroup, S[bh][i][j] = (qbar_i . kbar_j) / sqrt(D),
+// on the fp64 matrix cores: each wave owns a 32x32 quarter as 2x2 tiles of
+// v_mfma_f64_16x16x4f64 (A row i = lane%16, k = lane/16; B likewise; result
+// register r of a lane is row lane/16 + 4r, column lane%16), fed from LDS in
+// chunks of 32 along d.
+typedef __attribute__((ext_vector_type(4))) double f64x4;
+
 __global__ __launch_bounds__(256) void scores_kernel(Geo g, const double *qbar, const double *kbar,
                                                      double *S) {
     __shared__ double qs[64][33];
     __shared__ double ks[64][33];
     const int j0 = blockIdx.x * 64, i0 = blockIdx.y * 64, bh = blockIdx.z;
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wy = w >> 1, wx = w & 1;
+    const int l16 = lane & 15, kq = lane >> 4;
     const int Nb = g.Nb;
     const double *qb = qbar + (int64_t)bh * Nb * g.D;
     const double *kb = kbar + (int64_t)bh * Nb * g.D;
-    double acc[4][4];
+    f64x4 acc[2][2];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+        for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
     for (int d0 = 0; d0 < g.D; d0 += 32) {
         for (int e = threadIdx.x; e < 64 * 32; e += 256) {
             const int r = e >> 5, cc = e & 31;
@@ -166,31 +172,32 @@ __global__ __launch_bounds__(256) void scores_kernel(Geo g, const double *qbar, 
             ks[r][cc] = (j0 + r < Nb) ? kb[(int64_t)(j0 + r) * g.D + d0 + cc] : 0.0;
         }
         __syncthreads();
-#pragma unroll 8
-        for (int kk = 0; kk < 32; ++kk) {
-            double av[4], bv[4];
 #pragma unroll
-            for (int a = 0; a < 4; ++a) av[a] = qs[ty + 16 * a][kk];
+        for (int kk = 0; kk < 32; kk += 4) {
+            double av[2], bv[2];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) bv[b] = ks[tx + 16 * b][kk];
+            for (int a = 0; a < 2; ++a) av[a] = qs[32 * wy + 16 * a + l16][kk + kq];
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+            for (int b = 0; b < 2; ++b) bv[b] = ks[32 * wx + 16 * b + l16][kk + kq];
 #pragma unroll
-                for (int b = 0; b < 4; ++b) acc[a][b] = fma(av[a], bv[b], acc[a][b]);
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
         }
         __syncthreads();
     }
     const double sq = sqrt((double)g.D);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        const int i = i0 + ty + 16 * a;
-        if (i >= Nb) continue;
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int j = j0 + tx + 16 * b;
-            if (j < Nb) S[((int64_t)bh * Nb + i) * Nb + j] = acc[a][b] / sq;
+        for (int b = 0; b < 2; ++b) {
+            const int j = j0 + 32 * wx + 16 * b + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = i0 + 32 * wy + 16 * a + kq + 4 * r;
+                if (i < Nb && j < Nb) S[((int64_t)bh * Nb + i) * Nb + j] = acc[a][b][r] / sq;
+            }
         }
-    }
 }
 
 // ------------------------------------------------------------ row_select
