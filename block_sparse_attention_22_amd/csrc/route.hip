@@ -214,6 +214,38 @@ __device__ inline bool before(double pa, int ia, double pb, int ib) {
 
 constexpr int kRowsPerGroup = 4;
 
+// The 32-bit word of lane ^ LM (LM a power of two below 64): quad
+// permutations (DPP) for 1 and 2, the bit-mode lane swizzle for 4 to 16,
+// an LDS permute for 32.
+template <int LM>
+__device__ __forceinline__ int xor_lane(int x) {
+    if constexpr (LM == 1) return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    else if constexpr (LM == 2) return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    else if constexpr (LM < 32) return __builtin_amdgcn_ds_swizzle(x, (LM << 10) | 0x1F);  // and 31, xor LM
+    else return __shfl_xor(x, 32, 64);
+}
+
+template <int LM>
+__device__ __forceinline__ double xor_lane_d(double x) {
+    const int lo = xor_lane<LM>(__double2loint(x)), hi = xor_lane<LM>(__double2hiint(x));
+    return __hiloint2double(hi, lo);
+}
+
+// One bitonic stage whose partner entries live in lane ^ LM (same register).
+template <int LM, int E>
+__device__ __forceinline__ void cross_stage(double *v, int *id, int lane, int e0, int k) {
+    const bool lower = (lane & LM) == 0;
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+        const bool up = ((e0 + r) & k) == 0;
+        const double ov = xor_lane_d<LM>(v[r]);
+        const int oi = xor_lane<LM>(id[r]);
+        const bool take = before(ov, oi, v[r], id[r]) != (lower != up);
+        v[r] = take ? ov : v[r];
+        id[r] = take ? oi : id[r];
+    }
+}
+
 template <int E>
 __global__ __launch_bounds__(64 * kRowsPerGroup) void row_select_kernel(Geo g, double *SP, int32_t *order,
                                                                         int32_t *base, double p, int kmin) {
@@ -252,16 +284,13 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void row_select_kernel(Geo g, d
     // rather than divergent branches.
     for (int k = 2; k <= NKP; k <<= 1) {
         for (int j = k >> 1; j >= E; j >>= 1) {
-            const int lm = j / E;
-            const bool lower = (lane & lm) == 0;
-#pragma unroll
-            for (int r = 0; r < E; ++r) {
-                const bool up = ((e0 + r) & k) == 0;
-                const double ov = __shfl_xor(v[r], lm, 64);
-                const int oi = __shfl_xor(id[r], lm, 64);
-                const bool take = before(ov, oi, v[r], id[r]) != (lower != up);
-                v[r] = take ? ov : v[r];
-                id[r] = take ? oi : id[r];
+            switch (j / E) {      // wave-uniform
+                case 1: cross_stage<1, E>(v, id, lane, e0, k); break;
+                case 2: cross_stage<2, E>(v, id, lane, e0, k); break;
+                case 4: cross_stage<4, E>(v, id, lane, e0, k); break;
+                case 8: cross_stage<8, E>(v, id, lane, e0, k); break;
+                case 16: cross_stage<16, E>(v, id, lane, e0, k); break;
+                default: cross_stage<32, E>(v, id, lane, e0, k); break;
             }
         }
 #pragma unroll
