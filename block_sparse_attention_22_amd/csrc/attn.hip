@@ -5,13 +5,18 @@
 // counterpart of the pages' Runtime Load Balancing (section 3: attention
 // latency follows the largest workload, so long work is spread out).
 //
-//   plan_kernel      rows -> work items; rows longer than a chunk size are
-//                    split so that no item dominates a compute unit's share
-//   attn_bf16_kernel persistent workgroups pull items from a queue; per item
-//                    an online-softmax flash loop over the kept key blocks with
-//                    bf16 MFMA (v_mfma_f32_32x32x16_bf16) for Q K^T and P V
-//   attn_f32_kernel  the same contract in float32 arithmetic (small problems)
-//   combine_kernel   log-sum-exp merge of a split row's partial results
+//   plan_kernel           rows -> work items; rows longer than a chunk size
+//                         are split so that no item dominates a compute
+//                         unit's share
+//   pack_kv_kernel        block-major K and V^T copies (bf16, d = 128)
+//   attn_bf16_d128_kernel bf16, d = 128: two persistent workgroups per CU
+//                         pull items from per-XCD queues; per item an
+//                         online-softmax flash loop over the kept key blocks,
+//                         64 keys per step, K/V^T streamed by LDS-DMA, bf16
+//                         MFMA (v_mfma_f32_32x32x16_bf16) for Q K^T and P V
+//   attn_bf16_kernel      the same for d = 64 (K/V staged through registers)
+//   attn_f32_kernel       the same contract in float32 arithmetic
+//   combine_kernel        log-sum-exp merge of a split row's partial results
 //
 // MFMA data layout (32x32x16, wave64): the kernel computes S^T = K Q^T so that
 // each lane owns one query (column) and 16 keys per 32-key subtile.  The K
