@@ -330,3 +330,25 @@ def test_hilbert_edge_cases(dev, grid, p, kmin, budget, dtype, d, B, strided):
         assert np.all(counts == nb)
     if p < 1e-6:
         assert np.all(counts == min(nb, max(kmin, 1)))
+
+
+def test_maximum_block_count(dev):
+    """The largest supported list width: 2,048 key blocks per row (the row sort
+    then has no padding at all), one head; lists against the oracle, outputs
+    on sampled rows."""
+    grid, tile = (8, 128, 128), (1, 8, 8)          # 8 x 16 x 16 = 2048 blocks of 64 tokens
+    assert fva.num_blocks(grid, tile) == 2048
+    q, k, v = _small_case(grid, tile, 1, 128, "bf16", 90, scale=2.0)
+    lay = BlockLayout(grid, tile)
+    qn, kn, vn = (to_numpy(t) for t in (q, k, v))
+    ref = routing.route(qn, kn, lay, 0.8, 3, ("frac", 0.05))
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    lists = fva.route(qd, kd, 0.8, 3, ("frac", 0.05), grid=grid, tile=tile)
+    g = gpu_lists_to_host(lists)
+    rep = compare_lists(g, ref, 0.8, ("frac", 0.05), lay, 1, 1)
+    assert rep["exact_rows"] + rep["excused_count_rows"] + rep["excused_tie_rows"] >= rep["rows"]
+    o = fva.sparse_attn(qd, kd, vd, lists)
+    torch.cuda.synchronize()
+    rows = {0: np.sort(np.random.default_rng(91).choice(2048, 24, replace=False))}
+    err = attention_error(o, qn, kn, vn, lay, g["row_ptr"], g["col_idx"], rows=rows)
+    assert err <= TOL["bf16"], err
