@@ -358,15 +358,34 @@ __global__ __launch_bounds__(256) void head_total_kernel(Geo g, const int32_t *b
 constexpr int kAugThreads = 1024;
 constexpr int kAugRows = 2;            // rows per thread: Nb <= 2048
 
-// First position in [lo, hi) of a descending sorted row whose bit pattern is
-// below t (every position before it holds a value >= t).
-__device__ inline int first_below(const double *row, int lo, int hi, uint64_t t) {
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (double_bits(row[mid]) >= t) lo = mid + 1;
-        else hi = mid;
+// For the 15 thresholds t_v = x | (v << sh), v = 1..15: the first position
+// in [lo, hi) of a descending sorted row whose bit pattern is below t_v
+// (every position before it holds a value >= t_v), written to pos[v].  The
+// 15 binary searches run side by side for a common number of halvings, with
+// every probe issued unconditionally (index clamped to the row, result kept
+// only while the search is open), so one step waits for one round of loads
+// instead of 15 dependent chains.
+__device__ inline void first_below15(const double *row, int lo, int hi, int last, uint64_t x, int sh,
+                                     int *pos) {
+    int a[16], c[16];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) { a[v] = lo; c[v] = hi; }
+    // each step leaves a bracket of n entries with at most floor(n / 2)
+    for (int len = hi - lo; len > 0; len >>= 1) {
+        uint64_t bits[16];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) bits[v] = double_bits(row[min((a[v] + c[v]) >> 1, last)]);
+#pragma unroll
+        for (int v = 1; v < 16; ++v) {
+            const int mid = (a[v] + c[v]) >> 1;
+            const bool open = a[v] < c[v];
+            const bool above = bits[v] >= (x | ((uint64_t)v << sh));
+            a[v] = (open && above) ? mid + 1 : a[v];
+            c[v] = (open && !above) ? mid : c[v];
+        }
     }
-    return lo;
+#pragma unroll
+    for (int v = 1; v < 16; ++v) pos[v] = a[v];
 }
 
 // One workgroup per (batch, head).  Chooses the A_h candidates (positions
@@ -421,9 +440,8 @@ __global__ __launch_bounds__(kAugThreads) void augment_kernel(Geo g, const doubl
         for (int q = 0; q < kAugRows; ++q) {
             pos[q][0] = hi[q];
             const double *row = SP + ((int64_t)bh * Nb + (q < nr ? r0 + q : 0)) * Nb;
-#pragma unroll
-            for (int v = 1; v < 16; ++v)
-                pos[q][v] = (q < nr) ? first_below(row, lo[q], hi[q], x | ((uint64_t)v << sh)) : 0;
+            // rows past nr have lo = hi = 0: no step runs and every pos is 0
+            first_below15(row, lo[q], hi[q], Nb - 1, x, sh, pos[q]);
         }
 #pragma unroll
         for (int v = 1; v < 16; ++v) {
