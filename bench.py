@@ -302,10 +302,15 @@ def main():
     imb, busy = fva.per_cu_imbalance(ctas, ncu)
     counts = np.diff(rp)
     C = info.chunk_blocks
+    # items in the plan's order: heads by kept blocks, densest first (ties to
+    # the lower head), rows of a head in order
+    per_head = counts.reshape(w.B * w.H, nb)
+    head_order = sorted(range(w.B * w.H), key=lambda bh: (-int(per_head[bh].sum()), bh))
     item_costs = []
-    for c in counts:
-        n = 1 if c <= C else -(-int(c) // C)
-        item_costs += [c / n] * n
+    for bh in head_order:
+        for c in per_head[bh]:
+            n = 1 if c <= C else -(-int(c) // C)
+            item_costs += [c / n] * n
     pred_imb = simulate_queue(item_costs, info.num_ctas)
     dens = counts.reshape(w.B * w.H, nb).sum(axis=1) / (nb * nb)
     base_dens = lists.base_count[: len(counts)].cpu().numpy().reshape(w.B * w.H, nb).sum(axis=1) / (nb * nb)

@@ -10,7 +10,8 @@
 //                         unit's share
 //   pack_kv_kernel        block-major K and V^T copies (bf16, d = 128)
 //   attn_bf16_d128_kernel bf16, d = 128: two persistent workgroups per CU
-//                         pull items from per-XCD queues; per item an
+//                         pull items from per-XCD queues (runs of 8 items
+//                         dealt round robin to the 8 XCDs); per item an
 //                         online-softmax flash loop over the kept key blocks,
 //                         64 keys per step, K/V^T streamed by LDS-DMA, bf16
 //                         MFMA (v_mfma_f32_32x32x16_bf16) for Q K^T and P V
@@ -99,21 +100,31 @@ __device__ inline int next_item(PlanHeader *hdr, int *s_item) {
     return it;
 }
 
-// Per-XCD queues: the item list (rows in order) is cut into 8 equal ranges;
-// range q is served first by the workgroups on XCD q, so neighbouring rows,
-// which keep many of the same key blocks, share one L2.  A workgroup whose
-// range is empty moves on to the next range.  cur_q: the range this
+// Per-XCD queues.  The item list is dealt to the 8 queues in runs of kRun
+// consecutive items: queue q holds runs q, q + 8, q + 16, ...  A workgroup
+// serves the queue of its own XCD first, so each run of neighbouring rows
+// (which keep many of the same key blocks) shares one L2, while all XCDs
+// move through the list, and hence through the same heads, together, so a
+// head's keys and values are shared in the Infinity Cache.  A workgroup
+// whose queue is empty moves on to the next one.  cur_q: the queue this
 // workgroup is draining (starts at its XCD).
+constexpr int kRun = 8;
+
 __device__ inline int next_item_xcd(PlanHeader *hdr, int n_items, int &cur_q, int *s_item) {
     if (threadIdx.x == 0) {
         int *qs = hdr->queue;
         int it = n_items;
+        const int rounds = n_items / (8 * kRun), rest = n_items - rounds * 8 * kRun;
         for (int k = 0; k < 8; ++k) {
             const int q = cur_q & 7;
-            const int lo = (int)((int64_t)n_items * q / 8), hi = (int)((int64_t)n_items * (q + 1) / 8);
-            if (__hip_atomic_load(&qs[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < hi - lo) {
+            // items of queue q: (m * 8 + q) * kRun + w, w < kRun, below n_items
+            const int cnt = rounds * kRun + min(kRun, max(0, rest - q * kRun));
+            if (__hip_atomic_load(&qs[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < cnt) {
                 const int t = atomicAdd(&qs[q], 1);
-                if (lo + t < hi) { it = lo + t; break; }
+                if (t < cnt) {
+                    it = ((t / kRun) * 8 + q) * kRun + t % kRun;
+                    break;
+                }
             }
             ++cur_q;
         }
@@ -892,13 +903,35 @@ __device__ inline int chunks_of(int cnt, int C) { return (cnt > C) ? (cnt + C - 
 // none (INT_MAX) or automatic max(16, ceil(total / (8 * num_ctas))), which
 // keeps every item at most 1/8 of a workgroup's average share; a longer row
 // is cut into ceil(cnt / C) near-equal chunks, each a work item with its own
-// partial slot.  Items stay in (b, h, i) order so concurrently running
-// workgroups read the same head's keys and values.
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(int R, const int32_t *row_ptr, int chunk_mode,
+// partial slot.  Heads are emitted densest first (by kept blocks, ties to the
+// lower (b, h); in (b, h) order when there are more than kPlanThreads heads),
+// rows of a head in order: the long items of dense heads start early and the
+// short items of sparse heads fill the end of the queues, and concurrently
+// running workgroups read the same head's keys and values.
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(int R, int Nb, const int32_t *row_ptr, int chunk_mode,
                                                             int num_ctas, int cap_items, int cap_parts,
                                                             PlanHeader *hdr, WorkItem *items, SplitRow *splits) {
     __shared__ int tmp[kPlanThreads];
+    __shared__ int head_at[kPlanThreads];   // emission position -> (b, h)
     const int tid = threadIdx.x;
+    const int BH = R / Nb;
+    const bool by_density = BH <= kPlanThreads;
+    if (by_density) {
+        int mine = 0;
+        if (tid < BH) {
+            mine = row_ptr[(tid + 1) * Nb] - row_ptr[tid * Nb];
+            tmp[tid] = mine;
+        }
+        __syncthreads();
+        if (tid < BH) {
+            int rank = 0;
+            for (int h2 = 0; h2 < BH; ++h2) rank += (tmp[h2] > mine || (tmp[h2] == mine && h2 < tid)) ? 1 : 0;
+            head_at[rank] = tid;
+        }
+        __syncthreads();
+    }
+    // row emitted at position v
+    auto row_at = [&](int v) { return by_density ? head_at[v / Nb] * Nb + v % Nb : v; };
     const int seg = (R + kPlanThreads - 1) / kPlanThreads;
     const int r0 = min(R, tid * seg), r1 = min(R, r0 + seg);
     const int64_t total = row_ptr[R] - row_ptr[0];
@@ -911,7 +944,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int R, const int32_t
     int li, lp, ls;
     for (int attempt = 0; attempt < 2; ++attempt) {
         li = 0; lp = 0; ls = 0;
-        for (int r = r0; r < r1; ++r) {
+        for (int v = r0; v < r1; ++v) {
+            const int r = row_at(v);
             const int n = chunks_of(row_ptr[r + 1] - row_ptr[r], C);
             li += n;
             if (n > 1) { lp += n; ls += 1; }
@@ -928,7 +962,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int R, const int32_t
     item = plan_scan(li, tmp, &dummy);
     part = plan_scan(lp, tmp, &dummy);
     spl = plan_scan(ls, tmp, &dummy);
-    for (int r = r0; r < r1; ++r) {
+    for (int v = r0; v < r1; ++v) {
+        const int r = row_at(v);
         const int b0 = row_ptr[r], cnt = row_ptr[r + 1] - b0;
         const int n = chunks_of(cnt, C);
         if (n == 1) {
@@ -1011,7 +1046,7 @@ size_t packed_kv_bytes(const Geo &g) {
 
 hipError_t launch_plan(const Geo &g, const int32_t *row_ptr, int chunk_mode, int num_ctas, int cap_items,
                        int cap_parts, PlanHeader *hdr, WorkItem *items, SplitRow *splits, hipStream_t s) {
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, g.BH * g.Nb, row_ptr, chunk_mode, num_ctas,
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, g.BH * g.Nb, g.Nb, row_ptr, chunk_mode, num_ctas,
                        cap_items, cap_parts, hdr, items, splits);
     return hipGetLastError();
 }
