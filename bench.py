@@ -306,11 +306,32 @@ def main():
     # the lower head), rows of a head in order
     per_head = counts.reshape(w.B * w.H, nb)
     head_order = sorted(range(w.B * w.H), key=lambda bh: (-int(per_head[bh].sum()), bh))
+    # neighbouring query blocks of <= 64 tokens run as one item over the union
+    # of their lists when it holds at most C blocks (bf16, d = 128 only)
+    lead = set()
+    if info.n_row_pairs > 0:
+        small, i = sizes <= 64, 0
+        while i < nb - 1:
+            if small[i] and small[i + 1]:
+                lead.add(i)
+                i += 2
+            else:
+                i += 1
     item_costs = []
     for bh in head_order:
-        for c in per_head[bh]:
+        i = 0
+        while i < nb:
+            if i in lead:
+                r = bh * nb + i
+                union = len(np.union1d(ci[rp[r]:rp[r + 1]], ci[rp[r + 1]:rp[r + 2]]))
+                if union <= C:
+                    item_costs.append(union)
+                    i += 2
+                    continue
+            c = per_head[bh][i]
             n = 1 if c <= C else -(-int(c) // C)
             item_costs += [c / n] * n
+            i += 1
     pred_imb = simulate_queue(item_costs, info.num_ctas)
     dens = counts.reshape(w.B * w.H, nb).sum(axis=1) / (nb * nb)
     base_dens = lists.base_count[: len(counts)].cpu().numpy().reshape(w.B * w.H, nb).sum(axis=1) / (nb * nb)
@@ -353,7 +374,7 @@ def main():
         "per_cu_imbalance_predicted": round(pred_imb, 4),
         "distinct_cus": len(busy),
         "plan": {"n_items": info.n_items, "chunk_blocks": C, "n_split_rows": info.n_split_rows,
-                 "n_partials": info.n_partials, "num_ctas": info.num_ctas},
+                 "n_partials": info.n_partials, "n_row_pairs": info.n_row_pairs, "num_ctas": info.num_ctas},
         "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic() if (w.dtype == "bf16" and w.d == 128 and w.cid == 3 and not hilbert) else None,

@@ -56,12 +56,13 @@ class AttnOptions(ctypes.Structure):
 
 
 FVA_ATTN_PREPARED = 1
+FVA_ATTN_NO_ROW_PAIRS = 2
 
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [("n_items", ctypes.c_int32), ("chunk_blocks", ctypes.c_int32), ("n_split_rows", ctypes.c_int32),
                 ("n_partials", ctypes.c_int32), ("total_blocks", ctypes.c_int64), ("num_ctas", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("n_row_pairs", ctypes.c_int32)]
 
 
 class CtaStat(ctypes.Structure):
@@ -312,11 +313,12 @@ def _event_handle(e) -> int:
     return int(e.cuda_event)
 
 
-def attn_options(chunk_blocks: int = 0, num_ctas: int = 0, kernel_events=None, prepared: bool = False) -> AttnOptions:
+def attn_options(chunk_blocks: int = 0, num_ctas: int = 0, kernel_events=None, prepared: bool = False,
+                 row_pairs: bool = True) -> AttnOptions:
     o = AttnOptions()
     o.chunk_blocks = int(chunk_blocks)
     o.num_ctas = int(num_ctas)
-    o.flags = FVA_ATTN_PREPARED if prepared else 0
+    o.flags = (FVA_ATTN_PREPARED if prepared else 0) | (0 if row_pairs else FVA_ATTN_NO_ROW_PAIRS)
     if kernel_events is not None:
         e0, e1 = kernel_events
         o.kernel_events[0] = _event_handle(e0)
@@ -365,7 +367,7 @@ def attn_prepare(k: torch.Tensor, v: torch.Tensor, *, grid, tile=None, chunk_blo
 def sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lists: BlockLists, *,
                 out: Optional[torch.Tensor] = None, stats: Optional[torch.Tensor] = None,
                 chunk_blocks: int = 0, num_ctas: int = 0, kernel_events=None,
-                prepared: bool = False) -> torch.Tensor:
+                prepared: bool = False, row_pairs: bool = True) -> torch.Tensor:
     """Block-sparse attention over the kept blocks (fva_sparse_attn).
 
     ``stats``: optional uint8 device tensor of ``stats_bytes(...)`` bytes that
@@ -374,6 +376,8 @@ def sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lists: BlockL
     hipEvent_t ints) recorded right before and after the attention kernel.
     ``prepared``: ``attn_prepare(k, v, ...)`` already ran (ordered before
     this call) with the same tensors and options.
+    ``row_pairs``: let neighbouring query blocks of at most 64 tokens share a
+    work item (bf16, head_dim 128; off: FVA_ATTN_NO_ROW_PAIRS).
     """
     _check_qkv(q, k, v)
     lib = load_library()
@@ -382,7 +386,7 @@ def sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lists: BlockL
         out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
     if out.stride() != q.stride() or out.dtype != q.dtype:
         raise ValueError("out must match q's strides and dtype")
-    opts = attn_options(chunk_blocks, num_ctas, kernel_events, prepared)
+    opts = attn_options(chunk_blocks, num_ctas, kernel_events, prepared, row_pairs)
     wsb = lib.fva_attn_workspace_bytes(ctypes.byref(prob), ctypes.byref(opts))
     if wsb == 0:
         raise FvaError(FVA_ERR_INVALID_ARG, "fva_attn_workspace_bytes")

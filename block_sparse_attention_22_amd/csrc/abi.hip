@@ -137,12 +137,35 @@ RouteWs route_layout(const Geo &g) {
 // -------------------------------------------------------- attn workspace
 struct AttnPlanSizes {
     int num_ctas, cap_items, cap_parts, cap_splits;
+    int max_pairs;   // query-block pairs per (batch, head) the workspace holds
 };
+
+// Query blocks with at most kPairTokens tokens, from the block geometry (the
+// device pairs at most half of them).  Tiles: per axis, n - 1 tiles of the
+// tile's extent and a last one of the remaining extent.
+int64_t small_query_blocks(const Geo &g) {
+    if (g.order) return (g.N - (int64_t)(g.Nb - 1) * kMaxSlots) <= kPairTokens ? 1 : 0;
+    const int G[3] = {g.T, g.Y, g.X}, E[3] = {g.tt, g.ty, g.tx}, n[3] = {g.nT, g.nY, g.nX};
+    int64_t cnt[3][2], ext[3][2];
+    for (int a = 0; a < 3; ++a) {
+        cnt[a][0] = n[a] - 1;
+        ext[a][0] = E[a];
+        cnt[a][1] = 1;
+        ext[a][1] = G[a] - (int64_t)(n[a] - 1) * E[a];
+    }
+    int64_t small = 0;
+    for (int t = 0; t < 2; ++t)
+        for (int y = 0; y < 2; ++y)
+            for (int x = 0; x < 2; ++x)
+                if (ext[0][t] * ext[1][y] * ext[2][x] <= kPairTokens) small += cnt[0][t] * cnt[1][y] * cnt[2][x];
+    return small;
+}
 
 fva_status attn_sizes(const Geo &g, const fva_attn_options *opts, AttnPlanSizes *s) {
     int chunk = 0, ctas = 0;
     if (opts) {
-        if (opts->reserved != 0 || (opts->flags & ~FVA_ATTN_PREPARED) != 0) return FVA_ERR_INVALID_ARG;
+        if (opts->reserved != 0 || (opts->flags & ~(FVA_ATTN_PREPARED | FVA_ATTN_NO_ROW_PAIRS)) != 0)
+            return FVA_ERR_INVALID_ARG;
         if ((opts->kernel_events[0] == nullptr) != (opts->kernel_events[1] == nullptr)) return FVA_ERR_INVALID_ARG;
         chunk = opts->chunk_blocks;
         ctas = opts->num_ctas;
@@ -159,6 +182,11 @@ fva_status attn_sizes(const Geo &g, const fva_attn_options *opts, AttnPlanSizes 
     else if (chunk == 0) parts = 16LL * ctas;        // automatic chunks: <= 2 * total / C <= 16 * ctas
     else parts = R * ((g.Nb + chunk - 1) / chunk);   // fixed chunks
     if (parts > INT32_MAX / 2) return FVA_ERR_INVALID_ARG;
+    // Room for the row pairs whatever the options, so that the layout (and
+    // the K/V copies of fva_attn_prepare) does not depend on them.
+    int64_t pairs = uses_packed_kv(g) ? small_query_blocks(g) / 2 : 0;
+    if ((int64_t)g.BH * pairs * g.Nb > INT32_MAX / 2) pairs = 0;
+    s->max_pairs = (int)pairs;
     s->num_ctas = ctas;
     s->cap_parts = (int)parts;
     s->cap_splits = (int)(parts / 2);
@@ -167,7 +195,8 @@ fva_status attn_sizes(const Geo &g, const fva_attn_options *opts, AttnPlanSizes 
 }
 
 struct AttnWs {
-    size_t tok, bsize, hdr, items, splits, part_o, part_ml, kp, vt, total;
+    size_t tok, bsize, hdr, items, splits, part_o, part_ml, kp, vt;
+    size_t role, first, n_pairs, ucol, ulen, total;
 };
 
 AttnWs attn_layout(const Geo &g, const AttnPlanSizes &s) {
@@ -183,6 +212,11 @@ AttnWs attn_layout(const Geo &g, const AttnPlanSizes &s) {
     w.part_ml = take((size_t)s.cap_parts * kMaxSlots * 2 * 4);
     w.kp = take(packed_kv_bytes(g));
     w.vt = take(packed_kv_bytes(g));
+    w.role = take((size_t)g.Nb * 4);
+    w.first = take((size_t)(s.max_pairs > 0 ? s.max_pairs : 1) * 4);
+    w.n_pairs = take(4);
+    w.ucol = take((size_t)g.BH * s.max_pairs * g.Nb * 4);
+    w.ulen = take((size_t)g.BH * s.max_pairs * 4);
     w.total = off;
     return w;
 }
@@ -316,11 +350,18 @@ fva_status fva_sparse_attn(const fva_problem *prob, const void *q, const void *k
     const int chunk = opts ? opts->chunk_blocks : 0;
     if (!(opts && (opts->flags & FVA_ATTN_PREPARED)))
         FVA_TRY_HIP(launch_pack_kv(g, k, v, (uint16_t *)(W + L.kp), (uint16_t *)(W + L.vt), s));
+    // Pairs of small query blocks, unless fixed chunks or the flag say otherwise.
+    const bool pair_rows = sz.max_pairs > 0 && chunk <= 0 && !(opts && (opts->flags & FVA_ATTN_NO_ROW_PAIRS));
+    const RowPairs rp{pair_rows ? sz.max_pairs : 0, (int32_t *)(W + L.role), (int32_t *)(W + L.first),
+                      (int32_t *)(W + L.n_pairs), (int32_t *)(W + L.ucol), (int32_t *)(W + L.ulen)};
     FVA_TRY_HIP(launch_slot_table(g, tok, bsize, s));
-    FVA_TRY_HIP(launch_plan(g, lists->row_ptr, chunk, sz.num_ctas, sz.cap_items, sz.cap_parts, hdr, items, splits, s));
+    FVA_TRY_HIP(launch_row_pairs(g, bsize, lists->row_ptr, lists->col_idx, rp, s));
+    FVA_TRY_HIP(launch_plan(g, lists->row_ptr, chunk, sz.num_ctas, sz.cap_items, sz.cap_parts, rp, hdr, items, splits,
+                            s));
     hipEvent_t ev0 = opts ? (hipEvent_t)opts->kernel_events[0] : nullptr;
     hipEvent_t ev1 = opts ? (hipEvent_t)opts->kernel_events[1] : nullptr;
-    FVA_TRY_HIP(launch_attention(g, q, k, v, o, lists->col_idx, tok, bsize, hdr, items, part_o, part_ml,
+    FVA_TRY_HIP(launch_attention(g, q, k, v, o, lists->row_ptr, lists->col_idx, rp.ucol, tok, bsize, hdr, items,
+                                 part_o, part_ml,
                                  (fva_cta_stat *)stats, (uint16_t *)(W + L.kp), (uint16_t *)(W + L.vt), sz.num_ctas,
                                  ev0, ev1, s));
     FVA_TRY_HIP(launch_combine(g, o, tok, bsize, hdr, splits, part_o, part_ml, sz.cap_splits, s));

@@ -57,7 +57,7 @@ struct AttnArgs {
     Geo g;
     const void *q, *k, *v;
     void *o;
-    const int32_t *col_idx, *tok, *bsize;
+    const int32_t *row_ptr, *col_idx, *ucol, *tok, *bsize;
     PlanHeader *hdr;
     const WorkItem *items;
     float *part_o, *part_ml;
@@ -635,11 +635,20 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
             const cptr_i32 ip = (cptr_i32)a.items + 4 * it;
             wi.row = ip[0]; wi.kb_begin = ip[1]; wi.kb_end = ip[2]; wi.part = ip[3];
         }
-        const int bh = wi.row / g.Nb, i = wi.row - (wi.row / g.Nb) * g.Nb;
+        const int bh = wi.row / g.Nb;
         const int64_t boff = (int64_t)(bh / g.H) * g.sb + (int64_t)(bh % g.H) * g.sh;
+        // A paired item runs two query blocks of at most 64 tokens: waves 0-1
+        // take the first (block i of the row), waves 2-3 the second; each
+        // wave pair computes only the blocks of the union list that carry
+        // its member bit.
+        const bool paired = wi.part <= -2;
+        const int grp = paired ? (wu >> 1) : 0;
+        const int i = grp ? -2 - wi.part : wi.row - bh * g.Nb;
+        const int part = paired ? -1 : wi.part;
+        const int qw = paired ? (wu & 1) : wu;      // this wave's 32-query group within its block
         const int n_i = ((cptr_i32)a.bsize)[i];
-        const bool active = (w * 32) < n_i;
-        const int qslot = w * 32 + l32;
+        const bool active = (qw * 32) < n_i;
+        const int qslot = qw * 32 + l32;
         const bool qvalid = qslot < n_i;
         const int qtok = a.tok[i * kMaxSlots + qslot];
         bf16x8 qf[8];
@@ -659,7 +668,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
             for (int r = 0; r < 16; ++r) acc[u][r] = 0.f;
         float m_run = -INFINITY, l_run = 0.f;
         const int nkb = wi.kb_end - wi.kb_begin;
-        const cptr_i32 cols = (cptr_i32)a.col_idx + wi.kb_begin;
+        const cptr_i32 cols = (cptr_i32)(paired ? a.ucol : a.col_idx) + wi.kb_begin;
+        // list entry -> block index; whether this wave pair computes it
+        const int mshift = 16 + grp;
+        auto mine = [&](int e) { return !paired || ((e >> mshift) & 1); };
         if (nkb > 0) {
             const int64_t head_packed = (int64_t)bh * g.Nb * kMaxSlots * 128;
             const __amdgpu_buffer_rsrc_t rkp = head_rsrc(Kp_all + head_packed, (int64_t)g.Nb * kMaxSlots * 256);
@@ -669,10 +681,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
             // tokens), half hh.  Block indices are read two blocks ahead and
             // sizes one block ahead (scalar loads), K/V one half ahead (DMA).
             int jj = 0, hh = 0;
-            int j = cols[0], nj = bsz[j];
-            int j1 = (nkb > 1) ? cols[1] : 0;
+            int e0 = cols[0];
+            int j = e0 & 0xffff, nj = bsz[j];
+            bool own = mine(e0);
+            int e1 = (nkb > 1) ? cols[1] : 0;
+            int j1 = e1 & 0xffff;
             int n1 = (nkb > 1) ? bsz[j1] : 0;
-            int j2 = (nkb > 2) ? cols[2] : 0;
+            int e2 = (nkb > 2) ? cols[2] : 0;
             auto lds_addr = [](const uint16_t *p) { return (uint32_t)(uintptr_t)(const lds_ptr_t)p; };
             dma_half(DmaHalf{lds_addr(Ks0) + seg0, lds_addr(Vs0) + seg0, rkp, rvt, j, 0}, dl);
             // One step of the stream: wait for the current stage, start the
@@ -690,14 +705,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
                 // it keeps the k-step loop free of branches).
                 const bool more = jn < nkb;
                 const DmaHalf dn{lds_addr(Kn) + seg0, lds_addr(Vn) + seg0, rkp, rvt, more ? jnext : j, more ? hn : hh};
-                if (active) half_tile(Kc, Vc, nj - hh * kHalf, qf, acc, m_run, l_run, c, h, oa, dn, dl);
+                if (active && own) half_tile(Kc, Vc, nj - hh * kHalf, qf, acc, m_run, l_run, c, h, oa, dn, dl);
                 else dma_half(dn, dl);
                 if (jn >= nkb) return false;
                 if (!same) {
                     jj = jn;
-                    j = j1; nj = n1;
-                    if (jj + 1 < nkb) { j1 = j2; n1 = bsz[j2]; }
-                    if (jj + 2 < nkb) j2 = cols[jj + 2];
+                    j = j1; nj = n1; own = mine(e1);
+                    if (jj + 1 < nkb) { e1 = e2; j1 = e2 & 0xffff; n1 = bsz[j1]; }
+                    if (jj + 2 < nkb) e2 = cols[jj + 2];
                 }
                 hh = hn;
                 return true;
@@ -709,7 +724,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
         }
         const float l = l_run + __shfl_xor(l_run, 32, 64);
         if (active && qvalid) {
-            if (wi.part < 0) {
+            if (part < 0) {
                 const float inv = (l > 0.f) ? 1.f / l : 0.f;
                 uint16_t *orow = O + boff + (int64_t)qtok * g.sn;
 #pragma unroll
@@ -722,7 +737,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
                                        pack_bf16(acc[u][4 * rg + 2] * inv, acc[u][4 * rg + 3] * inv));
                     }
             } else {
-                float *po = a.part_o + ((int64_t)wi.part * kMaxSlots + qslot) * 128;
+                float *po = a.part_o + ((int64_t)part * kMaxSlots + qslot) * 128;
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -732,14 +747,15 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
                             make_float4(acc[u][4 * rg], acc[u][4 * rg + 1], acc[u][4 * rg + 2], acc[u][4 * rg + 3]);
                     }
                 if (h == 0) {
-                    float *pm = a.part_ml + ((int64_t)wi.part * kMaxSlots + qslot) * 2;
+                    float *pm = a.part_ml + ((int64_t)part * kMaxSlots + qslot) * 2;
                     pm[0] = m_run;
                     pm[1] = l;
                 }
             }
         }
         ++n_done;
-        blocks_done += nkb;
+        // kept (query block, key block) pairs: a pair's two rows, else the range
+        blocks_done += paired ? ((cptr_i32)a.row_ptr)[wi.row + 2] - ((cptr_i32)a.row_ptr)[wi.row] : nkb;
     }
     write_stats(a, t0, n_done, blocks_done);
 }
@@ -876,6 +892,122 @@ __global__ __launch_bounds__(kMaxSlots, 1) void attn_f32_kernel(AttnArgs a) {
     write_stats(a, t0, n_done, blocks_done);
 }
 
+// ------------------------------------------------------------- row pairs
+constexpr int kPairThreads = 1024;   // two blocks per thread: Nb <= 2048
+
+// Inclusive scan of v[0 .. 2 * kPairThreads) under a commutative op with
+// identity `id`, entries 2t and 2t + 1 on thread t; tmp: kPairThreads ints.
+template <typename Op>
+__device__ inline void scan2(int *v, int *tmp, Op op, int id) {
+    const int t = threadIdx.x;
+    const int a = v[2 * t], b = op(a, v[2 * t + 1]);
+    tmp[t] = b;
+    __syncthreads();
+    for (int off = 1; off < kPairThreads; off <<= 1) {
+        const int y = (t >= off) ? tmp[t - off] : id;
+        __syncthreads();
+        tmp[t] = op(tmp[t], y);
+        __syncthreads();
+    }
+    const int before = (t > 0) ? tmp[t - 1] : id;
+    __syncthreads();
+    v[2 * t] = op(before, a);
+    v[2 * t + 1] = op(before, b);
+    __syncthreads();
+}
+
+// Single workgroup.  In every run of consecutive query blocks of at most
+// kPairTokens tokens, blocks (s, s + 1), (s + 2, s + 3), ... from the run's
+// first block s are paired (an odd run leaves its last block alone), up to
+// `cap` pairs.  Writes role, first and n_pairs (see RowPairs).
+__global__ __launch_bounds__(kPairThreads) void pair_table_kernel(int Nb, int cap, const int32_t *bsize,
+                                                                  int32_t *role, int32_t *first, int32_t *n_pairs) {
+    __shared__ int small[2 * kPairThreads];
+    __shared__ int start[2 * kPairThreads];
+    __shared__ int rank[2 * kPairThreads];
+    __shared__ int tmp[kPairThreads];
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int e = 2 * t + k;
+        small[e] = (e < Nb && bsize[e] <= kPairTokens) ? 1 : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int e = 2 * t + k;
+        start[e] = (small[e] && (e == 0 || !small[e - 1])) ? e : -1;
+    }
+    __syncthreads();
+    // for a small block: the first block of its run (the last run start at or before it)
+    scan2(start, tmp, [](int x, int y) { return max(x, y); }, -1);
+    auto leads = [&](int e) {
+        return e >= 0 && e + 1 < Nb && small[e] && small[e + 1] && ((e - start[e]) & 1) == 0;
+    };
+#pragma unroll
+    for (int k = 0; k < 2; ++k) rank[2 * t + k] = leads(2 * t + k) ? 1 : 0;
+    __syncthreads();
+    scan2(rank, tmp, [](int x, int y) { return x + y; }, 0);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int e = 2 * t + k;
+        if (e >= Nb) continue;
+        const int p = rank[e] - 1;   // pair index of e if it leads, else of the last leader before it
+        int rl = -1;
+        if (leads(e)) {
+            if (p < cap) {
+                rl = p;
+                first[p] = e;
+            }
+        } else if (leads(e - 1) && p < cap) {
+            rl = -2;
+        }
+        role[e] = rl;
+    }
+    if (t == 0) *n_pairs = min(rank[2 * kPairThreads - 1], cap);
+}
+
+// One wave per (pair, batch*head): the ascending union of the two rows' kept
+// blocks with their member bits, through one bitmap per row in LDS (64
+// words: Nb <= 2048); lane l emits the blocks of word l.
+__global__ __launch_bounds__(64) void pair_union_kernel(int Nb, int max_pairs, const int32_t *row_ptr,
+                                                        const int32_t *col_idx, const int32_t *first,
+                                                        const int32_t *n_pairs, int32_t *ucol, int32_t *ulen) {
+    __shared__ uint32_t bm[2][64];
+    const int p = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
+    if (p >= *n_pairs) return;
+    bm[0][lane] = 0u;
+    bm[1][lane] = 0u;
+    __syncthreads();
+    const int r0 = bh * Nb + first[p];
+    for (int m = 0; m < 2; ++m) {
+        const int b0 = row_ptr[r0 + m], b1 = row_ptr[r0 + m + 1];
+        for (int e = b0 + lane; e < b1; e += 64) {
+            const int j = col_idx[e];
+            atomicOr(&bm[m][j >> 5], 1u << (j & 31));
+        }
+    }
+    __syncthreads();
+    const uint32_t a = bm[0][lane], b = bm[1][lane];
+    uint32_t u = a | b;
+    const int c = __popc(u);
+    int incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+    }
+    const int slot = bh * max_pairs + p;
+    int32_t *dst = ucol + (int64_t)slot * Nb;
+    int o = incl - c;
+    while (u) {
+        const int bit = __ffs(u) - 1;
+        u &= u - 1;
+        dst[o++] = (lane * 32 + bit) | (int)(((a >> bit) & 1u) << 16) | (int)(((b >> bit) & 1u) << 17);
+    }
+    if (lane == 63) ulen[slot] = incl;
+}
+
 // ------------------------------------------------------------------ plan
 constexpr int kPlanThreads = 1024;
 
@@ -907,9 +1039,13 @@ __device__ inline int chunks_of(int cnt, int C) { return (cnt > C) ? (cnt + C - 
 // lower (b, h); in (b, h) order when there are more than kPlanThreads heads),
 // rows of a head in order: the long items of dense heads start early and the
 // short items of sparse heads fill the end of the queues, and concurrently
-// running workgroups read the same head's keys and values.
+// running workgroups read the same head's keys and values.  With row pairs
+// (role != null), a pair whose union list holds at most C blocks is one item
+// over that list, emitted at the place of its first block and never split;
+// a longer pair runs as two rows, so that they can still be split.
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int R, int Nb, const int32_t *row_ptr, int chunk_mode,
                                                             int num_ctas, int cap_items, int cap_parts,
+                                                            const int32_t *role, const int32_t *ulen, int max_pairs,
                                                             PlanHeader *hdr, WorkItem *items, SplitRow *splits) {
     __shared__ int tmp[kPlanThreads];
     __shared__ int head_at[kPlanThreads];   // emission position -> (b, h)
@@ -940,21 +1076,34 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int R, int Nb, const
     else if (chunk_mode > 0) C = chunk_mode;
     else C = (int)max((int64_t)16, (total + 8LL * num_ctas - 1) / (8LL * num_ctas));
 
-    int n_items = 0, n_parts = 0, n_splits = 0;
-    int li, lp, ls;
+    // role of row r's query block under the current C: -1 alone, -2 second
+    // of a pair, p >= 0 first of pair p
+    auto role_of = [&](int r) {
+        if (!role) return -1;
+        const int i = r % Nb, rl = role[i];
+        const int p = (rl >= 0) ? rl : (rl == -2 ? role[i - 1] : -1);
+        if (p < 0 || ulen[(r / Nb) * max_pairs + p] > C) return -1;
+        return rl;
+    };
+    int n_items = 0, n_parts = 0, n_splits = 0, n_pairs = 0;
+    int li, lp, ls, lq;
     for (int attempt = 0; attempt < 2; ++attempt) {
-        li = 0; lp = 0; ls = 0;
+        li = 0; lp = 0; ls = 0; lq = 0;
         for (int v = r0; v < r1; ++v) {
             const int r = row_at(v);
+            const int rl = role_of(r);
+            if (rl == -2) continue;
+            if (rl >= 0) { li += 1; lq += 1; continue; }
             const int n = chunks_of(row_ptr[r + 1] - row_ptr[r], C);
             li += n;
             if (n > 1) { lp += n; ls += 1; }
         }
-        int ti, tp, ts;
+        int ti, tp, ts, tq;
         plan_scan(li, tmp, &ti);
         plan_scan(lp, tmp, &tp);
         plan_scan(ls, tmp, &ts);
-        n_items = ti; n_parts = tp; n_splits = ts;
+        plan_scan(lq, tmp, &tq);
+        n_items = ti; n_parts = tp; n_splits = ts; n_pairs = tq;
         if (n_items <= cap_items && n_parts <= cap_parts) break;
         C = INT32_MAX;     // cannot happen for the automatic size; never overrun the workspace
     }
@@ -964,6 +1113,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int R, int Nb, const
     spl = plan_scan(ls, tmp, &dummy);
     for (int v = r0; v < r1; ++v) {
         const int r = row_at(v);
+        const int rl = role_of(r);
+        if (rl == -2) continue;
+        if (rl >= 0) {
+            const int slot = (r / Nb) * max_pairs + rl;
+            items[item++] = WorkItem{r, slot * Nb, slot * Nb + ulen[slot], -2 - (r % Nb + 1)};
+            continue;
+        }
         const int b0 = row_ptr[r], cnt = row_ptr[r + 1] - b0;
         const int n = chunks_of(cnt, C);
         if (n == 1) {
@@ -984,7 +1140,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int R, int Nb, const
         hdr->info.n_partials = n_parts;
         hdr->info.total_blocks = total;
         hdr->info.num_ctas = num_ctas;
-        hdr->info.reserved = 0;
+        hdr->info.n_row_pairs = n_pairs;
         for (int q = 0; q < 8; ++q) hdr->queue[q] = 0;
     }
 }
@@ -1045,9 +1201,22 @@ size_t packed_kv_bytes(const Geo &g) {
 }
 
 hipError_t launch_plan(const Geo &g, const int32_t *row_ptr, int chunk_mode, int num_ctas, int cap_items,
-                       int cap_parts, PlanHeader *hdr, WorkItem *items, SplitRow *splits, hipStream_t s) {
+                       int cap_parts, const RowPairs &rp, PlanHeader *hdr, WorkItem *items, SplitRow *splits,
+                       hipStream_t s) {
+    const bool pairs = rp.max_pairs > 0;
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, g.BH * g.Nb, g.Nb, row_ptr, chunk_mode, num_ctas,
-                       cap_items, cap_parts, hdr, items, splits);
+                       cap_items, cap_parts, pairs ? rp.role : nullptr, pairs ? rp.ulen : nullptr, rp.max_pairs, hdr,
+                       items, splits);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_pairs(const Geo &g, const int32_t *bsize, const int32_t *row_ptr, const int32_t *col_idx,
+                           const RowPairs &rp, hipStream_t s) {
+    if (rp.max_pairs <= 0) return hipSuccess;
+    hipLaunchKernelGGL(pair_table_kernel, dim3(1), dim3(kPairThreads), 0, s, g.Nb, rp.max_pairs, bsize, rp.role,
+                       rp.first, rp.n_pairs);
+    hipLaunchKernelGGL(pair_union_kernel, dim3(rp.max_pairs, g.BH), dim3(64), 0, s, g.Nb, rp.max_pairs, row_ptr,
+                       col_idx, rp.first, rp.n_pairs, rp.ucol, rp.ulen);
     return hipGetLastError();
 }
 
@@ -1061,14 +1230,16 @@ hipError_t launch_pack_kv(const Geo &g, const void *k, const void *v, uint16_t *
 }
 
 hipError_t launch_attention(const Geo &g, const void *q, const void *k, const void *v, void *o,
-                            const int32_t *col_idx, const int32_t *tok, const int32_t *bsize, PlanHeader *hdr,
+                            const int32_t *row_ptr, const int32_t *col_idx, const int32_t *ucol, const int32_t *tok,
+                            const int32_t *bsize,
+                            PlanHeader *hdr,
                             const WorkItem *items, float *part_o, float *part_ml, fva_cta_stat *stats,
                             uint16_t *kp, uint16_t *vt, int num_ctas, hipEvent_t ev0, hipEvent_t ev1,
                             hipStream_t s) {
     AttnArgs a;
     a.g = g;
     a.q = q; a.k = k; a.v = v; a.o = o;
-    a.col_idx = col_idx; a.tok = tok; a.bsize = bsize;
+    a.row_ptr = row_ptr; a.col_idx = col_idx; a.ucol = ucol; a.tok = tok; a.bsize = bsize;
     a.hdr = hdr; a.items = items;
     a.part_o = part_o; a.part_ml = part_ml;
     a.stats = stats;

@@ -25,9 +25,26 @@ struct Geo {
 };
 
 // One unit of attention work: query-block row `row` (= (b*H + h)*Nb + i),
-// key-block range [kb_begin, kb_end) of col_idx, partial slot or -1.
+// key-block range [kb_begin, kb_end) of col_idx, partial slot or -1.  A
+// paired item (part = -2 - i2) runs query blocks i and i2 of the same head
+// together over [kb_begin, kb_end) of the pair's union list.
 struct WorkItem {
     int32_t row, kb_begin, kb_end, part;
+};
+
+// Query blocks of at most kPairTokens tokens fill only two of the four
+// 32-query waves of the bf16 d = 128 kernel; neighbouring ones are paired
+// into one work item.  Per geometry: role[i] = pair index p for the first
+// block of pair p, -2 for its second block, -1 for an unpaired block;
+// first[p] = first block of pair p; *n_pairs.  Per (batch, head) and pair:
+// the union of the two rows' kept blocks, ascending, at
+// ucol + ((b*H + h) * max_pairs + p) * Nb, entry = j | member bits << 16
+// (bit 0: in the first block's list, bit 1: in the second's), length ulen.
+// max_pairs = 0: no pairing.
+constexpr int kPairTokens = 64;
+struct RowPairs {
+    int max_pairs;
+    int32_t *role, *first, *n_pairs, *ucol, *ulen;
 };
 
 // Split row bookkeeping for the combine step.
@@ -97,11 +114,14 @@ hipError_t launch_csr(const Geo &g, const int32_t *order, const int32_t *base, c
                       uint32_t *mask, hipStream_t s);
 
 // Attention (attn.hip)
+hipError_t launch_row_pairs(const Geo &g, const int32_t *bsize, const int32_t *row_ptr, const int32_t *col_idx,
+                           const RowPairs &rp, hipStream_t s);
 hipError_t launch_plan(const Geo &g, const int32_t *row_ptr, int chunk_mode, int num_ctas,
-                       int cap_items, int cap_parts, PlanHeader *hdr, WorkItem *items,
+                       int cap_items, int cap_parts, const RowPairs &rp, PlanHeader *hdr, WorkItem *items,
                        SplitRow *splits, hipStream_t s);
 hipError_t launch_attention(const Geo &g, const void *q, const void *k, const void *v, void *o,
-                            const int32_t *col_idx, const int32_t *tok, const int32_t *bsize,
+                            const int32_t *row_ptr, const int32_t *col_idx, const int32_t *ucol, const int32_t *tok,
+                            const int32_t *bsize,
                             PlanHeader *hdr, const WorkItem *items, float *part_o, float *part_ml,
                             fva_cta_stat *stats, uint16_t *kp, uint16_t *vt, int num_ctas, hipEvent_t ev0,
                             hipEvent_t ev1, hipStream_t s);

@@ -122,6 +122,7 @@ typedef struct {
 } fva_lists;
 
 #define FVA_ATTN_PREPARED 1
+#define FVA_ATTN_NO_ROW_PAIRS 2
 
 /* Balancer options for fva_sparse_attn; pass NULL for the defaults (all 0). */
 typedef struct {
@@ -135,7 +136,9 @@ typedef struct {
     int32_t num_ctas;
     /* FVA_ATTN_PREPARED: the workspace already holds the K/V copies that
      * fva_attn_prepare wrote for the same problem, k, v and options, so
-     * fva_sparse_attn skips them.  No other bit may be set. */
+     * fva_sparse_attn skips them.
+     * FVA_ATTN_NO_ROW_PAIRS: do not pair query blocks (see fva_sparse_attn).
+     * No other bit may be set. */
     int32_t flags;
     int32_t reserved;     /* must be 0 */
     /* Optional caller-owned hipEvent_t pair (both or neither): recorded on
@@ -153,7 +156,7 @@ typedef struct {
     int32_t n_partials;    /* partial results merged by the combine step */
     int64_t total_blocks;  /* kept (query block, key block) pairs */
     int32_t num_ctas;      /* persistent workgroups launched */
-    int32_t reserved;
+    int32_t n_row_pairs;   /* work items that ran two query blocks together */
 } fva_plan_info;
 
 typedef struct {
@@ -218,6 +221,17 @@ size_t fva_attn_stats_bytes(const fva_problem *prob, const fva_attn_options *opt
  * with no kept block yields zeros.  stats: NULL or a device buffer of
  * fva_attn_stats_bytes(prob, opts) bytes.  Only row_ptr and col_idx of
  * `lists` are read.
+ *
+ * Balancing (the one-GPU counterpart of the pages' Runtime Load Balancing,
+ * paperlayer.ai summary of FVAttn, section 3 "FVAttn Design": attention
+ * latency follows the largest workload): rows are cut into work items that
+ * persistent workgroups pull from queues (opts->chunk_blocks).  For bf16 and
+ * head_dim 128, unless FVA_ATTN_NO_ROW_PAIRS is set or chunk_blocks > 0, two
+ * neighbouring query blocks of one head that each hold at most 64 tokens
+ * (edge tiles) run as one work item over the union of their key lists, each
+ * block attending only to its own kept blocks, in ascending block order; such
+ * items are never split.  The results are those of the unpaired run (bit for
+ * bit when the columns are ascending).
  */
 fva_status fva_sparse_attn(const fva_problem *prob, const void *q, const void *k, const void *v,
                            const fva_lists *lists, void *o, void *ws, size_t ws_bytes, void *stats,

@@ -81,7 +81,10 @@ def test_attn_workspace_with_explicit_ctas(lib):
     o.flags = fva.FVA_ATTN_PREPARED     # a valid flag does not change the size
     assert lib.fva_attn_workspace_bytes(ctypes.byref(p), ctypes.byref(o)) == \
         lib.fva_attn_workspace_bytes(ctypes.byref(p), ctypes.byref(AttnOptions(-1, 256)))
-    o.flags = 2                         # unknown flag bit
+    o.flags = fva.FVA_ATTN_PREPARED | fva.FVA_ATTN_NO_ROW_PAIRS   # the layout ignores the flags
+    assert lib.fva_attn_workspace_bytes(ctypes.byref(p), ctypes.byref(o)) == \
+        lib.fva_attn_workspace_bytes(ctypes.byref(p), ctypes.byref(AttnOptions(-1, 256)))
+    o.flags = 4                         # unknown flag bit
     assert lib.fva_attn_workspace_bytes(ctypes.byref(p), ctypes.byref(o)) == 0
     o.flags = 0
     o.kernel_events[0] = 0x1000        # one event without the other

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import block_sparse_attention_22_amd as fva
-from oracle import BlockLayout, attention, routing
+from oracle import BlockLayout, HilbertLayout, attention, routing
 from workloads import WORKLOADS, make_inputs, sample_qblocks, tiny_random
 
 from parity import attention_error, compare_lists, gpu_lists_to_host, to_numpy
@@ -160,7 +160,7 @@ def test_balancer_does_not_change_results(dev, cid, dtype, chunks):
         info, _ = fva.parse_stats(st)
         R = w.B * w.H * lay.Nb
         if chunk == -1:
-            assert info.n_items == R and info.n_partials == 0
+            assert info.n_items == R - info.n_row_pairs and info.n_partials == 0
         if chunk in (1, 3):
             assert info.n_partials > 0 and info.n_items > R
             assert info.chunk_blocks == chunk
@@ -181,6 +181,89 @@ def test_balancer_does_not_change_results(dev, cid, dtype, chunks):
     qn, kn, vn = (to_numpy(t) for t in (q, k, v))
     for o in outs.values():
         assert attention_error(o, qn, kn, vn, lay, g["row_ptr"], g["col_idx"]) <= TOL[dtype]
+
+
+def _greedy_pairs(sizes):
+    """Pairs of neighbouring query blocks of at most 64 tokens, taken two by
+    two from the start of every run of such blocks."""
+    small = np.asarray(sizes) <= 64
+    n, i = 0, 0
+    while i < len(small) - 1:
+        if small[i] and small[i + 1]:
+            n, i = n + 1, i + 2
+        else:
+            i += 1
+    return n
+
+
+@pytest.mark.parametrize("case", ["config2", "all64_odd_run", "mixed_edges", "hilbert"])
+def test_row_pairs_match_unpaired(dev, case):
+    """Query blocks of at most 64 tokens paired into one work item give the
+    unpaired results bit for bit, and as many pairs as the greedy rule."""
+    hilbert = case == "hilbert"
+    if case == "config2":
+        w = WORKLOADS[2]
+        q, k, v, _ = make_inputs(w)
+        grid, tile, p, kmin, budget, B, H = w.grid, w.tile, w.p, w.kmin, w.budget, w.B, w.H
+    else:
+        grid, tile = {"all64_odd_run": ((3, 24, 40), (1, 8, 8)), "mixed_edges": ((5, 20, 20), (2, 8, 8)),
+                      "hilbert": ((5, 20, 20), None)}[case]
+        B, H = 2, 3
+        q, k, v = _small_case(grid, tile, H, 128, "bf16", 90, scale=2.0, B=B)
+        p, kmin, budget = 0.85, 2, ("frac", 0.2)
+    print(f"\n[pairs] {case}: grid {grid} tile {tile}", flush=True)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    order = fva.hilbert_order(grid, dev) if hilbert else None
+    blk = dict(grid=grid, order=order) if hilbert else dict(grid=grid, tile=tile)
+    lists = fva.route(qd, kd, p, kmin, budget, **blk)
+    outs, infos = {}, {}
+    for chunk in (-1, 0):          # rows never split / the automatic split the bench uses
+        for on in (True, False):
+            st = torch.zeros(fva.stats_bytes(qd, grid, tile, chunk_blocks=chunk, order=order), dtype=torch.uint8,
+                             device=dev)
+            outs[chunk, on] = fva.sparse_attn(qd, kd, vd, lists, stats=st, chunk_blocks=chunk, row_pairs=on)
+            torch.cuda.synchronize()
+            infos[chunk, on], _ = fva.parse_stats(st)
+    sizes = fva.block_sizes(grid, tile, ordered=hilbert)
+    expect = 0 if hilbert else B * H * _greedy_pairs(sizes)
+    for chunk in (-1, 0):
+        assert infos[chunk, False].n_row_pairs == 0
+    # without splitting, every pair runs as one item, replaces two items by
+    # one and changes no bit
+    assert infos[-1, True].n_row_pairs == expect
+    assert infos[-1, True].n_items == infos[-1, False].n_items - expect
+    assert torch.equal(outs[-1, True], outs[-1, False])
+    # with the automatic split, only pairs whose union fits the chunk size run
+    # together, and such an item replaces at least two
+    n0 = infos[0, True].n_row_pairs
+    assert 0 <= n0 <= expect
+    assert infos[0, True].n_items <= infos[0, False].n_items - n0
+    lay = HilbertLayout(grid) if hilbert else BlockLayout(grid, tile)
+    g = gpu_lists_to_host(lists)
+    qn, kn, vn = (to_numpy(t) for t in (q, k, v))
+    for chunk in (-1, 0):
+        err = attention_error(outs[chunk, True], qn, kn, vn, lay, g["row_ptr"], g["col_idx"])
+        assert err <= TOL["bf16"], (chunk, err)
+
+
+def test_row_pairs_with_descending_columns(dev):
+    """Unordered columns: a pair walks the union in ascending order, so the
+    sum order differs from the unpaired run; both stay within tolerance."""
+    grid, tile, B, H = (3, 24, 40), (1, 8, 8), 1, 2
+    q, k, v = _small_case(grid, tile, H, 128, "bf16", 95, scale=2.0, B=B)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    lists = fva.route(qd, kd, 0.8, 2, None, grid=grid, tile=tile)
+    g = gpu_lists_to_host(lists)
+    rp, ci = g["row_ptr"], g["col_idx"].copy()
+    for r in range(len(rp) - 1):
+        ci[rp[r]:rp[r + 1]] = ci[rp[r]:rp[r + 1]][::-1]
+    rev = fva.lists_from_csr(rp, ci, nq=lists.nq, grid=grid, tile=tile, device=dev)
+    lay = BlockLayout(grid, tile)
+    qn, kn, vn = (to_numpy(t) for t in (q, k, v))
+    for on in (True, False):
+        o = fva.sparse_attn(qd, kd, vd, rev, row_pairs=on)
+        torch.cuda.synchronize()
+        assert attention_error(o, qn, kn, vn, lay, rp, ci) <= TOL["bf16"]
 
 
 def test_empty_problem(dev):
