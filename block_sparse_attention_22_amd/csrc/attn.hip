@@ -5,13 +5,19 @@
 // counterpart of the pages' Runtime Load Balancing (section 3: attention
 // latency follows the largest workload, so long work is spread out).
 //
-//   plan_kernel           rows -> work items; rows longer than a chunk size
-//                         are split so that no item dominates a compute
-//                         unit's share
+//   pair_table_kernel     per geometry: pairs of neighbouring query blocks of
+//                         at most 64 tokens (two of the four waves each)
+//   pair_union_kernel     per pair and head: the union of the two rows' kept
+//                         blocks, with a member bit per row
+//   plan_kernel           rows -> work items, heads densest first; rows longer
+//                         than a chunk size are split so that no item
+//                         dominates a compute unit's share; a pair whose union
+//                         fits the chunk size is one item
 //   pack_kv_kernel        block-major K and V^T copies (bf16, d = 128)
 //   attn_bf16_d128_kernel bf16, d = 128: two persistent workgroups per CU
 //                         pull items from per-XCD queues (runs of 8 items
-//                         dealt round robin to the 8 XCDs); per item an
+//                         dealt round robin to the 8 XCDs); per item (one
+//                         query block, or a pair on waves 0-1 and 2-3) an
 //                         online-softmax flash loop over the kept key blocks,
 //                         64 keys per step, K/V^T streamed by LDS-DMA, bf16
 //                         MFMA (v_mfma_f32_32x32x16_bf16) for Q K^T and P V
