@@ -202,14 +202,26 @@ __global__ __launch_bounds__(256) void scores_kernel(Geo g, const double *qbar, 
 
 // ------------------------------------------------------------ row_select
 // One wave per (query block, batch*head) row, four rows per workgroup.  The
-// row (padded to a power of two NKP = 64*E, padding mass -1 so it sorts last)
-// lives in registers, E entries per lane, entry e = lane*E + r.  A bitonic
-// network orders it by (mass desc, index asc): strides below E exchange
-// registers inside a lane, larger strides exchange with lane ^ (stride/E).
-// Writes the sorted masses (in place), the matching key-block order and the
-// Top-p + floor count.
+// row (padded to a power of two NKP = 64*E with mass +0 and indices >= Nk,
+// which therefore sort after every real entry) lives in registers, E entries
+// per lane, entry e = lane*E + r.  A bitonic network orders it by (mass desc,
+// index asc): strides below E exchange registers inside a lane, larger
+// strides exchange with lane ^ (stride/E).  The network first runs on the
+// mass alone, compared as the integer of its bit pattern (one compare per
+// exchange; the masses are non-negative, so that order is the numeric one).
+// A row in which two neighbours of that result have the same mass and one of
+// them is a real entry is marked (base = -1) and left to a second launch
+// (EXACT) that sorts only such rows with the index as tie-break; two
+// launches keep one network per kernel.  Writes the sorted masses (in place),
+// the matching key-block order and the Top-p + floor count.
 __device__ inline bool before(double pa, int ia, double pb, int ib) {
     return (pa > pb) | ((pa == pb) & (ia < ib));     // bitwise: no short-circuit branch
+}
+
+template <bool EXACT>
+__device__ __forceinline__ bool precedes(double pa, int ia, double pb, int ib) {
+    if (EXACT) return before(pa, ia, pb, ib);
+    return __double_as_longlong(pa) > __double_as_longlong(pb);
 }
 
 constexpr int kRowsPerGroup = 4;
@@ -232,27 +244,77 @@ __device__ __forceinline__ double xor_lane_d(double x) {
 }
 
 // One bitonic stage whose partner entries live in lane ^ LM (same register).
-template <int LM, int E>
-__device__ __forceinline__ void cross_stage(double *v, int *id, int lane, int e0, int k) {
-    const bool lower = (lane & LM) == 0;
+// up: the direction of this lane's entries (the same for all of them, since
+// the merge width k of a cross-lane stage is at least 2E).
+template <int LM, int E, bool EXACT>
+__device__ __forceinline__ void cross_stage(double *v, int *id, int lane, bool up) {
+    const bool flip = ((lane & LM) == 0) != up;
 #pragma unroll
     for (int r = 0; r < E; ++r) {
-        const bool up = ((e0 + r) & k) == 0;
         const double ov = xor_lane_d<LM>(v[r]);
         const int oi = xor_lane<LM>(id[r]);
-        const bool take = before(ov, oi, v[r], id[r]) != (lower != up);
+        const bool take = precedes<EXACT>(ov, oi, v[r], id[r]) != flip;
         v[r] = take ? ov : v[r];
         id[r] = take ? oi : id[r];
     }
 }
 
-template <int E>
+// Compare-exchange of entries r and r + j of this lane, ascending (mass
+// desc, index asc) when up.
+template <bool EXACT>
+__device__ __forceinline__ void lane_cx(double *v, int *id, int r, int j, bool up) {
+    const double va = v[r], vb = v[r + j];
+    const int ia = id[r], ib = id[r + j];
+    const bool sw = precedes<EXACT>(vb, ib, va, ia) == up;
+    v[r] = sw ? vb : va;
+    v[r + j] = sw ? va : vb;
+    id[r] = sw ? ib : ia;
+    id[r + j] = sw ? ia : ib;
+}
+
+// The bitonic network over the whole row (see row_select_kernel).  Entry
+// e = e0 + r runs in direction up = ((e & k) == 0) in the merge of width k.
+// For k < E that is (r & k) == 0, a constant of the unrolled loops; for
+// k >= E it is (e0 & k) == 0, the same for all of a lane's entries.
+template <int E, bool EXACT>
+__device__ __forceinline__ void bitonic_row(double *v, int *id, int lane, int e0) {
+    constexpr int NKP = 64 * E;
+    // Exchanges are written as selects so that they compile to v_cndmask
+    // rather than divergent branches.
+#pragma unroll
+    for (int k = 2; k < E; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j >= 1; j >>= 1)
+#pragma unroll
+            for (int r = 0; r < E; ++r)
+                if (!(r & j)) lane_cx<EXACT>(v, id, r, j, (r & k) == 0);
+    for (int k = E; k <= NKP; k <<= 1) {
+        const bool up = (e0 & k) == 0;
+        for (int j = k >> 1; j >= E; j >>= 1) {
+            switch (j / E) {      // wave-uniform
+                case 1: cross_stage<1, E, EXACT>(v, id, lane, up); break;
+                case 2: cross_stage<2, E, EXACT>(v, id, lane, up); break;
+                case 4: cross_stage<4, E, EXACT>(v, id, lane, up); break;
+                case 8: cross_stage<8, E, EXACT>(v, id, lane, up); break;
+                case 16: cross_stage<16, E, EXACT>(v, id, lane, up); break;
+                default: cross_stage<32, E, EXACT>(v, id, lane, up); break;
+            }
+        }
+#pragma unroll
+        for (int j = E / 2; j >= 1; j >>= 1)
+#pragma unroll
+            for (int r = 0; r < E; ++r)
+                if (!(r & j)) lane_cx<EXACT>(v, id, r, j, up);
+    }
+}
+
+template <int E, bool EXACT>
 __global__ __launch_bounds__(64 * kRowsPerGroup) void row_select_kernel(Geo g, double *SP, int32_t *order,
                                                                         int32_t *base, double p, int kmin) {
-    constexpr int NKP = 64 * E;
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kRowsPerGroup + (threadIdx.x >> 6);
     if (row >= (int64_t)g.BH * g.Nb) return;
+    if (EXACT && base[row] >= 0) return;      // sorted by the first launch
     const int Nk = g.Nb;
     double *srow = SP + row * Nk;
     const int e0 = lane * E;
@@ -278,37 +340,22 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void row_select_kernel(Geo g, d
     }
     sum = wave_sum(sum);
 #pragma unroll
-    for (int r = 0; r < E; ++r) v[r] = (e0 + r < Nk) ? v[r] / sum : -1.0;   // padding sorts last
+    for (int r = 0; r < E; ++r) v[r] = (e0 + r < Nk) ? v[r] / sum : 0.0;   // padding: +0, index >= Nk
 
-    // Exchanges are written as selects so that they compile to v_cndmask
-    // rather than divergent branches.
-    for (int k = 2; k <= NKP; k <<= 1) {
-        for (int j = k >> 1; j >= E; j >>= 1) {
-            switch (j / E) {      // wave-uniform
-                case 1: cross_stage<1, E>(v, id, lane, e0, k); break;
-                case 2: cross_stage<2, E>(v, id, lane, e0, k); break;
-                case 4: cross_stage<4, E>(v, id, lane, e0, k); break;
-                case 8: cross_stage<8, E>(v, id, lane, e0, k); break;
-                case 16: cross_stage<16, E>(v, id, lane, e0, k); break;
-                default: cross_stage<32, E>(v, id, lane, e0, k); break;
-            }
-        }
+    bitonic_row<E, EXACT>(v, id, lane, e0);
+    if (!EXACT) {
+        // Equal neighbours (entry e, e + 1) with a real entry among them: the
+        // order the mass alone gave them may not be the index order.
+        bool tie = false;
 #pragma unroll
-        for (int j = E / 2; j >= 1; j >>= 1) {
-            if (j < k) {
-#pragma unroll
-                for (int r = 0; r < E; ++r) {
-                    if (r & j) continue;
-                    const bool up = ((e0 + r) & k) == 0;
-                    const double va = v[r], vb = v[r + j];
-                    const int ia = id[r], ib = id[r + j];
-                    const bool sw = before(vb, ib, va, ia) == up;
-                    v[r] = sw ? vb : va;
-                    v[r + j] = sw ? va : vb;
-                    id[r] = sw ? ib : ia;
-                    id[r + j] = sw ? ia : ib;
-                }
-            }
+        for (int r = 0; r + 1 < E; ++r)
+            tie |= (v[r] == v[r + 1]) & ((id[r] < Nk) | (id[r + 1] < Nk));
+        const double nv = __shfl_down(v[0], 1, 64);
+        const int ni = __shfl_down(id[0], 1, 64);
+        tie |= (lane < 63) & (v[E - 1] == nv) & ((id[E - 1] < Nk) | (ni < Nk));
+        if (__any(tie)) {
+            if (lane == 0) base[row] = -1;
+            return;
         }
     }
 
@@ -588,18 +635,18 @@ hipError_t launch_row_select(const Geo &g, double *SP, int32_t *order, int32_t *
     const int64_t R = (int64_t)g.BH * g.Nb;
     if (R == 0) return hipSuccess;
     const dim3 grid((unsigned)((R + kRowsPerGroup - 1) / kRowsPerGroup)), block(64 * kRowsPerGroup);
-    if (g.Nb <= 64)
-        hipLaunchKernelGGL(row_select_kernel<1>, grid, block, 0, s, g, SP, order, base, p, kmin);
-    else if (g.Nb <= 128)
-        hipLaunchKernelGGL(row_select_kernel<2>, grid, block, 0, s, g, SP, order, base, p, kmin);
-    else if (g.Nb <= 256)
-        hipLaunchKernelGGL(row_select_kernel<4>, grid, block, 0, s, g, SP, order, base, p, kmin);
-    else if (g.Nb <= 512)
-        hipLaunchKernelGGL(row_select_kernel<8>, grid, block, 0, s, g, SP, order, base, p, kmin);
-    else if (g.Nb <= 1024)
-        hipLaunchKernelGGL(row_select_kernel<16>, grid, block, 0, s, g, SP, order, base, p, kmin);
-    else
-        hipLaunchKernelGGL(row_select_kernel<32>, grid, block, 0, s, g, SP, order, base, p, kmin);
+    // the sort on the mass alone, then the exact sort of the rows it marked
+    for (int pass = 0; pass < 2; ++pass) {
+        auto go = [&](auto fast, auto exact) {
+            hipLaunchKernelGGL(pass == 0 ? fast : exact, grid, block, 0, s, g, SP, order, base, p, kmin);
+        };
+        if (g.Nb <= 64) go(row_select_kernel<1, false>, row_select_kernel<1, true>);
+        else if (g.Nb <= 128) go(row_select_kernel<2, false>, row_select_kernel<2, true>);
+        else if (g.Nb <= 256) go(row_select_kernel<4, false>, row_select_kernel<4, true>);
+        else if (g.Nb <= 512) go(row_select_kernel<8, false>, row_select_kernel<8, true>);
+        else if (g.Nb <= 1024) go(row_select_kernel<16, false>, row_select_kernel<16, true>);
+        else go(row_select_kernel<32, false>, row_select_kernel<32, true>);
+    }
     return hipGetLastError();
 }
 

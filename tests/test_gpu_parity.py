@@ -135,6 +135,40 @@ def test_edge_cases(dev, grid, tile, p, kmin, budget):
         assert np.all(counts == nb)
 
 
+@pytest.mark.parametrize("case", ["constant_keys", "duplicate_block"])
+def test_tied_masses_follow_block_order(dev, case):
+    """Equal routing masses are ordered by the lower block index (the routing
+    sort first orders by mass alone and re-sorts a row with ties exactly).
+    constant_keys: every mass of every row is equal, and p = 0.5 falls on a
+    sum that is exact in floating point; duplicate_block: key block 5 is a
+    copy of key block 2, so every row holds one tie."""
+    grid, tile, H = (4, 16, 16), (1, 8, 8), 2          # 16 blocks of 64 tokens
+    q, k, v = _small_case(grid, tile, H, 128, "bf16", 80, scale=2.0)
+    lay = BlockLayout(grid, tile)
+    if case == "constant_keys":
+        k = torch.full_like(k, 0.25)
+        p, kmin, budget = 0.5, 1, ("frac", 0.25)
+    else:
+        members = lay.members
+        k[:, :, torch.as_tensor(members[5])] = k[:, :, torch.as_tensor(members[2])]
+        p, kmin, budget = 0.8, 2, ("frac", 0.2)
+    qn, kn = to_numpy(q), to_numpy(k)
+    ref = routing.route(qn, kn, lay, p, kmin, budget)
+    lists = fva.route(q.to(dev), k.to(dev), p, kmin, budget, grid=grid, tile=tile)
+    g = gpu_lists_to_host(lists)
+    rep = compare_lists(g, ref, p, budget, lay, 1, H)
+    print(f"\n[ties] {case}: {rep}", flush=True)
+    assert rep["exact_rows"] == rep["rows"]
+    if case == "constant_keys":
+        counts = np.diff(g["row_ptr"]).reshape(H, lay.Nb)
+        base = lists.base_count[: H * lay.Nb].cpu().numpy().reshape(H, lay.Nb)
+        assert np.all(base == 8)                       # 8 of 16 equal masses reach 0.5
+        for h in range(H):                             # every row keeps a prefix of the block order
+            for i in range(lay.Nb):
+                cols = g["col_idx"][g["row_ptr"][h * lay.Nb + i]:g["row_ptr"][h * lay.Nb + i + 1]]
+                assert list(cols) == list(range(counts[h, i]))
+
+
 def test_batch_and_strided_views(dev):
     grid, tile = (3, 16, 24), (2, 8, 8)
     q, k, v = _small_case(grid, tile, 3, 128, "bf16", 70, scale=2.0, B=2)
