@@ -435,18 +435,36 @@ __device__ inline void first_below15(const double *row, int lo, int hi, int last
     for (int v = 1; v < 16; ++v) pos[v] = a[v];
 }
 
+// First position in [lo, hi) of a descending sorted row whose bit pattern is
+// below t.
+__device__ inline int first_below(const double *row, int lo, int hi, uint64_t t) {
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (double_bits(row[mid]) >= t) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+constexpr int kAugGather = 1024;   // bracket size from which tau is picked directly
+
 // One workgroup per (batch, head).  Chooses the A_h candidates (positions
 // r >= base_i of each row's sorted masses) with the largest mass, ties to
 // lower (i, j): a radix search over the IEEE bit pattern of the masses (four
-// bits per round, 15 thresholds at a time) finds the A_h-th largest mass
-// tau; rows take everything above tau, and the entries equal to tau go to
-// the lowest rows first (each row's equal entries are already in ascending j).
+// bits per round, 15 thresholds at a time) narrows a per-row bracket around
+// the A_h-th largest mass tau; once the brackets hold at most kAugGather
+// entries together, tau is picked among them directly (rank counting in
+// LDS) and each row is re-bracketed to its entries equal to tau.  Rows take
+// everything above tau, and the entries equal to tau go to the lowest rows
+// first (each row's equal entries are already in ascending j).
 __global__ __launch_bounds__(kAugThreads) void augment_kernel(Geo g, const double *SP, const int32_t *base,
                                                               int32_t *add, const int32_t *head_base,
                                                               int32_t *head_kept, int mode, double frac) {
     __shared__ int cnt[16];
     __shared__ int tmp[kAugThreads];
     __shared__ int ired[kAugThreads / 64];
+    __shared__ uint64_t gat[kAugGather];
+    __shared__ uint64_t tau_s;
     const int bh = blockIdx.x, tid = threadIdx.x;
     const int b = bh / g.H;
     const int Nb = g.Nb;
@@ -479,6 +497,7 @@ __global__ __launch_bounds__(kAugThreads) void augment_kernel(Geo g, const doubl
         hi[q] = (q < nr) ? Nb : 0;
     }
     uint64_t x = 0;
+    bool direct = false;
     for (int sh = 60; sh >= 0; sh -= 4) {
         if (tid < 16) cnt[tid] = 0;
         __syncthreads();
@@ -515,6 +534,53 @@ __global__ __launch_bounds__(kAugThreads) void augment_kernel(Geo g, const doubl
             lo[q] = nlo;
         }
         __syncthreads();
+        int br = 0;
+#pragma unroll
+        for (int q = 0; q < kAugRows; ++q) br += hi[q] - lo[q];
+        if (sh > 0 && block_reduce<kAugThreads>(br, ired, [](int a, int c) { return a + c; }) <= kAugGather) {
+            direct = true;
+            break;
+        }
+    }
+    if (direct) {
+        // tau is the (A - above)-th largest of the bracketed entries
+        int above = 0, inb = 0;
+#pragma unroll
+        for (int q = 0; q < kAugRows; ++q) {
+            above += (q < nr) ? lo[q] - m[q] : 0;
+            inb += hi[q] - lo[q];
+        }
+        const int rank_tau = A - block_reduce<kAugThreads>(above, ired, [](int a, int c) { return a + c; }) - 1;
+        if (tid == 0) tau_s = 0;     // overwritten below by the entry of rank rank_tau
+        int n_in;
+        int o = block_exclusive_scan<kAugThreads>(inb, tmp, &n_in);
+#pragma unroll
+        for (int q = 0; q < kAugRows; ++q) {
+            const double *row = SP + ((int64_t)bh * Nb + (q < nr ? r0 + q : 0)) * Nb;
+            for (int pp = lo[q]; pp < hi[q]; ++pp) gat[o++] = double_bits(row[pp]);
+        }
+        __syncthreads();
+        // rank of entry e in (bits desc, e asc): unique, so one entry has rank_tau
+        for (int e = tid; e < n_in; e += kAugThreads) {
+            const uint64_t ve = gat[e];
+            int rk = 0;
+            for (int f = 0; f < n_in; ++f) {
+                const uint64_t vf = gat[f];
+                rk += (vf > ve) | ((vf == ve) & (f < e));
+            }
+            if (rk == rank_tau) tau_s = ve;
+        }
+        __syncthreads();
+        const uint64_t tau = tau_s;
+#pragma unroll
+        for (int q = 0; q < kAugRows; ++q) {
+            if (q < nr) {
+                const double *row = SP + ((int64_t)bh * Nb + r0 + q) * Nb;
+                const int nlo = first_below(row, lo[q], hi[q], tau + 1);   // first entry <= tau
+                hi[q] = first_below(row, nlo, hi[q], tau);                   // first entry < tau
+                lo[q] = nlo;
+            }
+        }
     }
     // lo..hi now brackets the entries equal to tau; before lo: above tau.
     int gt = 0, eq = 0;
