@@ -126,11 +126,22 @@ __global__ __launch_bounds__(256) void pool_kernel(Geo g, const T *x, double *ou
     const BlockTokens bt = block_tokens(g, b);
     const int n = bt.n;
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int r = grp; r < n; r += G) {
-        float f[8];
-        load8(base + (int64_t)bt.token(r) * g.sn, f);
+    // rows grp, grp + G, ... below n (G >= 16, so at most kMaxSlots / 16 of
+    // them): all loads first, then the sums in row order; rows past n load
+    // the block's first token and add nothing
+    constexpr int kRowsPerThread = kMaxSlots / 16;
+    float f[kRowsPerThread][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += (double)f[e];
+    for (int u = 0; u < kRowsPerThread; ++u) {
+        const int r = grp + u * G;
+        load8(base + (int64_t)bt.token(r < n ? r : 0) * g.sn, f[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kRowsPerThread; ++u) {
+        if (grp + u * G < n) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += (double)f[u][e];
+        }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[grp * g.D + c * 8 + e] = acc[e];
