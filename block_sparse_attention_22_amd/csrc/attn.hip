@@ -768,8 +768,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
 
 // Block-major copies for the d=128 kernel, one workgroup per (block,
 // batch*head): Kp[(bh*Nb + j)*128 + slot][128] and Vt[(bh*Nb + j)*128 + dd][128
-// slots], slots past the block's tokens zero.  Each thread moves 8 slots of one
-// 16-byte chunk and transposes its 8x8 V tile in registers.
+// slots], slots past the block's tokens zero.  K: 16 lanes move one 256-byte
+// row.  V: each thread transposes an 8x8 tile (8 slots of one 16-byte chunk)
+// in registers, with the threads of a wave on 4 chunks x all 16 slot groups,
+// so that every V^T store of a wave fills whole rows.
 __global__ __launch_bounds__(256) void pack_kv_kernel(Geo g, const uint16_t *K, const uint16_t *V,
                                                       uint16_t *Kp, uint16_t *Vt) {
     const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
@@ -784,13 +786,15 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(Geo g, const uint16_t *K, 
         const int slot = hi + 16 * m;
         kx[m] = *reinterpret_cast<const u32x4 *>(K + hoff + (int64_t)bt.token(slot) * g.sn + c16 * 8);
     }
-    // V: slots 8*hi .. 8*hi+7 of the 16-byte chunk c16 (16 lanes read one
-    // token row), transposed in registers to 8 dd rows x 8 slots.
+    // V: slots 8*hv .. 8*hv+7 of the 16-byte chunk cv, transposed in
+    // registers to 8 dd rows x 8 slots; a wave covers 4 chunks x 16 slot
+    // groups, so each of its stores fills whole 256-byte V^T rows.
+    const int hv = tid & 15, cv = tid >> 4;
     u32x4 in[8];
 #pragma unroll
     for (int s8 = 0; s8 < 8; ++s8) {
-        const int slot = 8 * hi + s8;
-        in[s8] = *reinterpret_cast<const u32x4 *>(V + hoff + (int64_t)bt.token(slot) * g.sn + c16 * 8);
+        const int slot = 8 * hv + s8;
+        in[s8] = *reinterpret_cast<const u32x4 *>(V + hoff + (int64_t)bt.token(slot) * g.sn + cv * 8);
     }
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
@@ -800,15 +804,15 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(Geo g, const uint16_t *K, 
     }
 #pragma unroll
     for (int s8 = 0; s8 < 8; ++s8)
-        if (8 * hi + s8 >= bt.n) in[s8] = u32x4{0, 0, 0, 0};
+        if (8 * hv + s8 >= bt.n) in[s8] = u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const int dd = 8 * c16 + e;
+        const int dd = 8 * cv + e;
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
         u32x4 o;
 #pragma unroll
         for (int w = 0; w < 4; ++w) o[w] = __builtin_amdgcn_perm(in[2 * w + 1][e >> 1], in[2 * w][e >> 1], sel);
-        *reinterpret_cast<u32x4 *>(Vt + pblk + dd * kMaxSlots + 8 * hi) = o;
+        *reinterpret_cast<u32x4 *>(Vt + pblk + dd * kMaxSlots + 8 * hv) = o;
     }
 }
 
