@@ -1021,25 +1021,40 @@ __global__ __launch_bounds__(64) void pair_union_kernel(int Nb, int max_pairs, c
 // ------------------------------------------------------------------ plan
 constexpr int kPlanThreads = 1024;
 
-template <typename T>
-__device__ inline T plan_scan(T x, T *tmp, T *total) {
-    const int t = threadIdx.x;
-    __syncthreads();
-    tmp[t] = x;
-    __syncthreads();
-    for (int off = 1; off < kPlanThreads; off <<= 1) {
-        T y = (t >= off) ? tmp[t - off] : T(0);
-        __syncthreads();
-        tmp[t] += y;
-        __syncthreads();
-    }
-    T incl = tmp[t];
-    *total = tmp[kPlanThreads - 1];
-    __syncthreads();
-    return incl - x;
-}
-
 __device__ inline int chunks_of(int cnt, int C) { return (cnt > C) ? (cnt + C - 1) / C : 1; }
+
+// Exclusive scan of four per-thread counts over the workgroup (wave scans by
+// lane shuffles, then the 16 wave totals through LDS): x becomes the sum over
+// the threads before this one, tot the sum over all.
+__device__ inline void plan_scan4(int *x, int *tot, int (*wsum)[4]) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    int incl[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) incl[c] = x[c];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int y = __shfl_up(incl[c], off, 64);
+            if (lane >= off) incl[c] += y;
+        }
+    __syncthreads();
+    if (lane == 63)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) wsum[w][c] = incl[c];
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        int before = 0, all = 0;
+        for (int i = 0; i < kPlanThreads / 64; ++i) {
+            const int v = wsum[i][c];
+            before += (i < w) ? v : 0;
+            all += v;
+        }
+        tot[c] = all;
+        x[c] = before + incl[c] - x[c];
+    }
+}
 
 // Single workgroup.  Cost of a row = its kept key blocks.  chunk C: fixed,
 // none (INT_MAX) or automatic max(16, ceil(total / (8 * num_ctas))), which
@@ -1095,32 +1110,28 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int R, int Nb, const
         if (p < 0 || ulen[(r / Nb) * max_pairs + p] > C) return -1;
         return rl;
     };
+    __shared__ int wsum[kPlanThreads / 64][4];
     int n_items = 0, n_parts = 0, n_splits = 0, n_pairs = 0;
-    int li, lp, ls, lq;
+    int cnt4[4], tot4[4];        // this thread's items, partial slots, split rows, pairs
     for (int attempt = 0; attempt < 2; ++attempt) {
-        li = 0; lp = 0; ls = 0; lq = 0;
+        int li = 0, lp = 0, ls = 0, lq = 0;
+#pragma unroll 4
         for (int v = r0; v < r1; ++v) {
             const int r = row_at(v);
             const int rl = role_of(r);
-            if (rl == -2) continue;
-            if (rl >= 0) { li += 1; lq += 1; continue; }
-            const int n = chunks_of(row_ptr[r + 1] - row_ptr[r], C);
-            li += n;
-            if (n > 1) { lp += n; ls += 1; }
+            const int n = (rl < 0) ? chunks_of(row_ptr[r + 1] - row_ptr[r], C) : 0;
+            li += (rl >= 0) ? 1 : (rl == -1 ? n : 0);
+            lq += (rl >= 0) ? 1 : 0;
+            lp += (rl == -1 && n > 1) ? n : 0;
+            ls += (rl == -1 && n > 1) ? 1 : 0;
         }
-        int ti, tp, ts, tq;
-        plan_scan(li, tmp, &ti);
-        plan_scan(lp, tmp, &tp);
-        plan_scan(ls, tmp, &ts);
-        plan_scan(lq, tmp, &tq);
-        n_items = ti; n_parts = tp; n_splits = ts; n_pairs = tq;
+        cnt4[0] = li; cnt4[1] = lp; cnt4[2] = ls; cnt4[3] = lq;
+        plan_scan4(cnt4, tot4, wsum);
+        n_items = tot4[0]; n_parts = tot4[1]; n_splits = tot4[2]; n_pairs = tot4[3];
         if (n_items <= cap_items && n_parts <= cap_parts) break;
         C = INT32_MAX;     // cannot happen for the automatic size; never overrun the workspace
     }
-    int item = 0, part = 0, spl = 0, dummy;
-    item = plan_scan(li, tmp, &dummy);
-    part = plan_scan(lp, tmp, &dummy);
-    spl = plan_scan(ls, tmp, &dummy);
+    int item = cnt4[0], part = cnt4[1], spl = cnt4[2];
     for (int v = r0; v < r1; ++v) {
         const int r = row_at(v);
         const int rl = role_of(r);
