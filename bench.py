@@ -40,7 +40,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # 256 CUs * 2.4 GHz * 4096 bf16 flop/clk/CU, dense
-PEAK_F32_MFMA_TFLOPS = 157.3
+PEAK_F32_VALU_TFLOPS = 157.3   # fp32 vector, packed (256 CUs * 2.4 GHz * 256 flop/clk/CU)
 KERNEL_NAME = "attn_bf16_d128_kernel"     # the dominant kernel of the path (bf16, d=128)
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_bf16_d128_kernel_720p_layer_traffic.md")
 KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_attention_22_amd", "csrc", "attn.hip")
@@ -338,6 +338,13 @@ def main():
 
     tflops = flops / (ms_step * 1e-3) / 1e12
     kernel_tflops = flops / (kernel_ms * 1e-3) / 1e12
+    # the kernel that runs and the peak of its arithmetic: bf16 on the matrix
+    # cores, float32 on the vector ALUs
+    if w.dtype == "bf16":
+        bound, peak = "mfma", PEAK_BF16_TFLOPS
+        kernel_name = KERNEL_NAME if w.d == 128 else "attn_bf16_kernel<64>"
+    else:
+        bound, peak, kernel_name = "alu", PEAK_F32_VALU_TFLOPS, f"attn_f32_kernel<{w.d}>"
     res = {
         "metric": "ms/layer + effective sparse TFLOP/s (% bf16 MFMA peak) at 75,600 tok x 40 heads",
         "value": round(tflops, 2),
@@ -375,10 +382,10 @@ def main():
         "distinct_cus": len(busy),
         "plan": {"n_items": info.n_items, "chunk_blocks": C, "n_split_rows": info.n_split_rows,
                  "n_partials": info.n_partials, "n_row_pairs": info.n_row_pairs, "num_ctas": info.num_ctas},
-        "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": bound, "achieved": round(kernel_tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(kernel_tflops / peak, 4),
                      "traffic": measured_traffic() if (w.dtype == "bf16" and w.d == 128 and w.cid == 3 and not hilbert) else None,
-                     "kernel": KERNEL_NAME, "per_launch_flop": flops, "avg_launch_ms": round(kernel_ms, 4)},
+                     "kernel": kernel_name, "per_launch_flop": flops, "avg_launch_ms": round(kernel_ms, 4)},
     }
     if not args.no_dense:
         # Dense comparator: the same kernel on every key block (p = 1), after
