@@ -176,13 +176,28 @@ __global__ __launch_bounds__(256) void scores_kernel(Geo g, const double *qbar, 
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+    // chunk d0 of both tiles: element e = threadIdx.x + 256 m is row e / 32,
+    // column e % 32; the next chunk is loaded into registers while the
+    // current one is multiplied
+    double qr[8], kr[8];
+    auto load_chunk = [&](int d0) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int e = threadIdx.x + 256 * m, r = e >> 5, cc = e & 31;
+            qr[m] = (i0 + r < Nb) ? qb[(int64_t)(i0 + r) * g.D + d0 + cc] : 0.0;
+            kr[m] = (j0 + r < Nb) ? kb[(int64_t)(j0 + r) * g.D + d0 + cc] : 0.0;
+        }
+    };
+    load_chunk(0);
     for (int d0 = 0; d0 < g.D; d0 += 32) {
-        for (int e = threadIdx.x; e < 64 * 32; e += 256) {
-            const int r = e >> 5, cc = e & 31;
-            qs[r][cc] = (i0 + r < Nb) ? qb[(int64_t)(i0 + r) * g.D + d0 + cc] : 0.0;
-            ks[r][cc] = (j0 + r < Nb) ? kb[(int64_t)(j0 + r) * g.D + d0 + cc] : 0.0;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int e = threadIdx.x + 256 * m, r = e >> 5, cc = e & 31;
+            qs[r][cc] = qr[m];
+            ks[r][cc] = kr[m];
         }
         __syncthreads();
+        if (d0 + 32 < g.D) load_chunk(d0 + 32);
 #pragma unroll
         for (int kk = 0; kk < 32; kk += 4) {
             double av[2], bv[2];
