@@ -232,22 +232,15 @@ __global__ __launch_bounds__(256) void scores_kernel(Geo g, const double *qbar, 
 // which therefore sort after every real entry) lives in registers, E entries
 // per lane, entry e = lane*E + r.  A bitonic network orders it by (mass desc,
 // index asc): strides below E exchange registers inside a lane, larger
-// strides exchange with lane ^ (stride/E).  The network first runs on the
-// mass alone, compared as the integer of its bit pattern (one compare per
-// exchange; the masses are non-negative, so that order is the numeric one).
-// A row in which two neighbours of that result have the same mass and one of
-// them is a real entry is marked (base = -1) and left to a second launch
-// (EXACT) that sorts only such rows with the index as tie-break; two
-// launches keep one network per kernel.  Writes the sorted masses (in place),
-// the matching key-block order and the Top-p + floor count.
+// strides exchange with lane ^ (stride/E).  The first launch sorts one
+// 64-bit integer key per entry (a truncated mass above the index, built in
+// row_select_kernel) and checks the result against the exact masses; a row
+// that fails the check is marked (base = -1) and left to a second launch
+// (EXACT) that sorts only such rows on (mass, index) pairs; two launches
+// keep one network per kernel.  Writes the sorted masses (in place), the
+// matching key-block order and the Top-p + floor count.
 __device__ inline bool before(double pa, int ia, double pb, int ib) {
     return (pa > pb) | ((pa == pb) & (ia < ib));     // bitwise: no short-circuit branch
-}
-
-template <bool EXACT>
-__device__ __forceinline__ bool precedes(double pa, int ia, double pb, int ib) {
-    if (EXACT) return before(pa, ia, pb, ib);
-    return __double_as_longlong(pa) > __double_as_longlong(pb);
 }
 
 constexpr int kRowsPerGroup = 4;
@@ -272,14 +265,14 @@ __device__ __forceinline__ double xor_lane_d(double x) {
 // One bitonic stage whose partner entries live in lane ^ LM (same register).
 // up: the direction of this lane's entries (the same for all of them, since
 // the merge width k of a cross-lane stage is at least 2E).
-template <int LM, int E, bool EXACT>
+template <int LM, int E>
 __device__ __forceinline__ void cross_stage(double *v, int *id, int lane, bool up) {
     const bool flip = ((lane & LM) == 0) != up;
 #pragma unroll
     for (int r = 0; r < E; ++r) {
         const double ov = xor_lane_d<LM>(v[r]);
         const int oi = xor_lane<LM>(id[r]);
-        const bool take = precedes<EXACT>(ov, oi, v[r], id[r]) != flip;
+        const bool take = before(ov, oi, v[r], id[r]) != flip;
         v[r] = take ? ov : v[r];
         id[r] = take ? oi : id[r];
     }
@@ -287,11 +280,10 @@ __device__ __forceinline__ void cross_stage(double *v, int *id, int lane, bool u
 
 // Compare-exchange of entries r and r + j of this lane, ascending (mass
 // desc, index asc) when up.
-template <bool EXACT>
 __device__ __forceinline__ void lane_cx(double *v, int *id, int r, int j, bool up) {
     const double va = v[r], vb = v[r + j];
     const int ia = id[r], ib = id[r + j];
-    const bool sw = precedes<EXACT>(vb, ib, va, ia) == up;
+    const bool sw = before(vb, ib, va, ia) == up;
     v[r] = sw ? vb : va;
     v[r + j] = sw ? va : vb;
     id[r] = sw ? ib : ia;
@@ -302,7 +294,7 @@ __device__ __forceinline__ void lane_cx(double *v, int *id, int r, int j, bool u
 // e = e0 + r runs in direction up = ((e & k) == 0) in the merge of width k.
 // For k < E that is (r & k) == 0, a constant of the unrolled loops; for
 // k >= E it is (e0 & k) == 0, the same for all of a lane's entries.
-template <int E, bool EXACT>
+template <int E>
 __device__ __forceinline__ void bitonic_row(double *v, int *id, int lane, int e0) {
     constexpr int NKP = 64 * E;
     // Exchanges are written as selects so that they compile to v_cndmask
@@ -313,24 +305,81 @@ __device__ __forceinline__ void bitonic_row(double *v, int *id, int lane, int e0
         for (int j = k >> 1; j >= 1; j >>= 1)
 #pragma unroll
             for (int r = 0; r < E; ++r)
-                if (!(r & j)) lane_cx<EXACT>(v, id, r, j, (r & k) == 0);
+                if (!(r & j)) lane_cx(v, id, r, j, (r & k) == 0);
     for (int k = E; k <= NKP; k <<= 1) {
         const bool up = (e0 & k) == 0;
         for (int j = k >> 1; j >= E; j >>= 1) {
             switch (j / E) {      // wave-uniform
-                case 1: cross_stage<1, E, EXACT>(v, id, lane, up); break;
-                case 2: cross_stage<2, E, EXACT>(v, id, lane, up); break;
-                case 4: cross_stage<4, E, EXACT>(v, id, lane, up); break;
-                case 8: cross_stage<8, E, EXACT>(v, id, lane, up); break;
-                case 16: cross_stage<16, E, EXACT>(v, id, lane, up); break;
-                default: cross_stage<32, E, EXACT>(v, id, lane, up); break;
+                case 1: cross_stage<1, E>(v, id, lane, up); break;
+                case 2: cross_stage<2, E>(v, id, lane, up); break;
+                case 4: cross_stage<4, E>(v, id, lane, up); break;
+                case 8: cross_stage<8, E>(v, id, lane, up); break;
+                case 16: cross_stage<16, E>(v, id, lane, up); break;
+                default: cross_stage<32, E>(v, id, lane, up); break;
             }
         }
 #pragma unroll
         for (int j = E / 2; j >= 1; j >>= 1)
 #pragma unroll
             for (int r = 0; r < E; ++r)
-                if (!(r & j)) lane_cx<EXACT>(v, id, r, j, up);
+                if (!(r & j)) lane_cx(v, id, r, j, up);
+    }
+}
+
+// The same network on one 64-bit key per entry, descending.
+template <int LM>
+__device__ __forceinline__ uint64_t xor_lane_u64(uint64_t x) {
+    const uint32_t lo = (uint32_t)xor_lane<LM>((int)(uint32_t)x), hi = (uint32_t)xor_lane<LM>((int)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <int LM, int E>
+__device__ __forceinline__ void cross_stage_key(uint64_t *key, int lane, bool up) {
+    const bool flip = ((lane & LM) == 0) != up;
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+        const uint64_t ok = xor_lane_u64<LM>(key[r]);
+        key[r] = ((ok > key[r]) != flip) ? ok : key[r];
+    }
+}
+
+template <int E>
+__device__ __forceinline__ void bitonic_keys(uint64_t *key, int lane, int e0) {
+    constexpr int NKP = 64 * E;
+#pragma unroll
+    for (int k = 2; k < E; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j >= 1; j >>= 1)
+#pragma unroll
+            for (int r = 0; r < E; ++r)
+                if (!(r & j)) {
+                    const uint64_t a = key[r], b = key[r + j];
+                    const bool sw = (b > a) == ((r & k) == 0);
+                    key[r] = sw ? b : a;
+                    key[r + j] = sw ? a : b;
+                }
+    for (int k = E; k <= NKP; k <<= 1) {
+        const bool up = (e0 & k) == 0;
+        for (int j = k >> 1; j >= E; j >>= 1) {
+            switch (j / E) {      // wave-uniform
+                case 1: cross_stage_key<1, E>(key, lane, up); break;
+                case 2: cross_stage_key<2, E>(key, lane, up); break;
+                case 4: cross_stage_key<4, E>(key, lane, up); break;
+                case 8: cross_stage_key<8, E>(key, lane, up); break;
+                case 16: cross_stage_key<16, E>(key, lane, up); break;
+                default: cross_stage_key<32, E>(key, lane, up); break;
+            }
+        }
+#pragma unroll
+        for (int j = E / 2; j >= 1; j >>= 1)
+#pragma unroll
+            for (int r = 0; r < E; ++r)
+                if (!(r & j)) {
+                    const uint64_t a = key[r], b = key[r + j];
+                    const bool sw = (b > a) == up;
+                    key[r] = sw ? b : a;
+                    key[r + j] = sw ? a : b;
+                }
     }
 }
 
@@ -368,18 +417,38 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void row_select_kernel(Geo g, d
 #pragma unroll
     for (int r = 0; r < E; ++r) v[r] = (e0 + r < Nk) ? v[r] / sum : 0.0;   // padding: +0, index >= Nk
 
-    bitonic_row<E, EXACT>(v, id, lane, e0);
-    if (!EXACT) {
-        // Equal neighbours (entry e, e + 1) with a real entry among them: the
-        // order the mass alone gave them may not be the index order.
-        bool tie = false;
+    if (EXACT) {
+        bitonic_row<E>(v, id, lane, e0);
+    } else {
+        // Key = the high word of the mass's bit pattern (sign, exponent and
+        // 20 mantissa bits: order-preserving for masses >= 0, with no
+        // underflow) above the complemented index: one integer compare per
+        // exchange orders by (truncated mass desc, index asc).  The exact
+        // masses wait in LDS.  Two neighbours of the result that share a
+        // high word can still be out of exact order; a row with any such pair
+        // is left to the exact launch.
+        __shared__ double pl[kRowsPerGroup][64 * E];
+        double *prow = pl[threadIdx.x >> 6];
+        uint64_t key[E];
 #pragma unroll
-        for (int r = 0; r + 1 < E; ++r)
-            tie |= (v[r] == v[r + 1]) & ((id[r] < Nk) | (id[r + 1] < Nk));
+        for (int r = 0; r < E; ++r) {
+            prow[e0 + r] = v[r];
+            key[r] = ((uint64_t)__double2hiint(v[r]) << 32) | (uint32_t)~(uint32_t)(e0 + r);
+        }
+        bitonic_keys<E>(key, lane, e0);
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+            id[r] = (int)~(uint32_t)key[r];
+            v[r] = (id[r] < Nk) ? prow[id[r]] : 0.0;
+        }
+        // Equal exact masses already sit in index order (the low word), so
+        // the only misorder is a smaller mass before a larger one.
+        bool bad = false;
+#pragma unroll
+        for (int r = 0; r + 1 < E; ++r) bad |= v[r] < v[r + 1];
         const double nv = __shfl_down(v[0], 1, 64);
-        const int ni = __shfl_down(id[0], 1, 64);
-        tie |= (lane < 63) & (v[E - 1] == nv) & ((id[E - 1] < Nk) | (ni < Nk));
-        if (__any(tie)) {
+        bad |= (lane < 63) & (v[E - 1] < nv);
+        if (__any(bad)) {
             if (lane == 0) base[row] = -1;
             return;
         }

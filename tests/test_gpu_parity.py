@@ -169,6 +169,37 @@ def test_tied_masses_follow_block_order(dev, case):
                 assert list(cols) == list(range(counts[h, i]))
 
 
+def test_near_tied_masses_take_the_exact_order(dev):
+    """Two masses that agree in their leading 20 mantissa bits but not below:
+    key block 5 is key block 2 with one coordinate of one token raised by one
+    float32 ulp, towards a query coordinate that is positive everywhere, so
+    block 5 holds the larger mass in every row by a relative 1e-8 or so.  The
+    routing sort's first pass orders on a truncated key, which puts the lower
+    index first; the exact order must win.  With p below the top mass and no
+    augmentation each row keeps exactly one block, so a misorder changes it."""
+    grid, tile, H = (4, 16, 16), (1, 8, 8), 2          # 16 blocks of 64 tokens
+    q, k, v = _small_case(grid, tile, H, 128, "fp32", 90)
+    lay = BlockLayout(grid, tile)
+    m2, m5 = (torch.as_tensor(lay.members[j]) for j in (2, 5))
+    q[..., 0] = q[..., 0].abs() + 1.0
+    k[:, :, m2, 0] = 20.0
+    k[:, :, m5] = k[:, :, m2]
+    k[:, :, m5[0], 0] = float(np.nextafter(np.float32(20.0), np.float32(np.inf)))
+    p, kmin, budget = 0.2, 1, ("none", 0.0)
+    qn, kn = to_numpy(q), to_numpy(k)
+    ref = routing.route(qn, kn, lay, p, kmin, budget)
+    for hd in ref["heads"][0]:
+        P = hd["P"]
+        assert np.all(P[:, 5] > P[:, 2]) and np.all(np.abs(P[:, 5] / P[:, 2] - 1) < 1e-7)
+        assert np.all(hd["base"] == 1)
+    lists = fva.route(q.to(dev), k.to(dev), p, kmin, budget, grid=grid, tile=tile)
+    g = gpu_lists_to_host(lists)
+    rep = compare_lists(g, ref, p, budget, lay, 1, H)
+    print(f"\n[near ties] {rep}", flush=True)
+    assert rep["exact_rows"] == rep["rows"]
+    assert np.all(np.diff(g["row_ptr"]) == 1) and np.all(g["col_idx"][: H * lay.Nb] == 5)
+
+
 def test_batch_and_strided_views(dev):
     grid, tile = (3, 16, 24), (2, 8, 8)
     q, k, v = _small_case(grid, tile, 3, 128, "bf16", 70, scale=2.0, B=2)
