@@ -138,7 +138,8 @@ def test_edge_cases(dev, grid, tile, p, kmin, budget):
 @pytest.mark.parametrize("case", ["constant_keys", "duplicate_block"])
 def test_tied_masses_follow_block_order(dev, case):
     """Equal routing masses are ordered by the lower block index (the routing
-    sort first orders by mass alone and re-sorts a row with ties exactly).
+    sort's keys carry the index below the mass, so exact ties come out in
+    index order from the first pass).
     constant_keys: every mass of every row is equal, and p = 0.5 falls on a
     sum that is exact in floating point; duplicate_block: key block 5 is a
     copy of key block 2, so every row holds one tie."""
@@ -169,22 +170,25 @@ def test_tied_masses_follow_block_order(dev, case):
                 assert list(cols) == list(range(counts[h, i]))
 
 
-def test_near_tied_masses_take_the_exact_order(dev):
+@pytest.mark.parametrize("grid,H,big", [((4, 16, 16), 2, 20.0), ((4, 160, 128), 1, 60.0)],
+                         ids=["16_blocks", "1280_blocks"])
+def test_near_tied_masses_take_the_exact_order(dev, grid, H, big):
     """Two masses that agree in their leading 20 mantissa bits but not below:
     key block 5 is key block 2 with one coordinate of one token raised by one
     float32 ulp, towards a query coordinate that is positive everywhere, so
     block 5 holds the larger mass in every row by a relative 1e-8 or so.  The
     routing sort's first pass orders on a truncated key, which puts the lower
     index first; the exact order must win.  With p below the top mass and no
-    augmentation each row keeps exactly one block, so a misorder changes it."""
-    grid, tile, H = (4, 16, 16), (1, 8, 8), 2          # 16 blocks of 64 tokens
+    augmentation each row keeps exactly one block, so a misorder changes it.
+    16 blocks sort one slot per lane, 1,280 blocks 32 slots per lane."""
+    tile = (1, 8, 8)                                   # blocks of 64 tokens
     q, k, v = _small_case(grid, tile, H, 128, "fp32", 90)
     lay = BlockLayout(grid, tile)
     m2, m5 = (torch.as_tensor(lay.members[j]) for j in (2, 5))
     q[..., 0] = q[..., 0].abs() + 1.0
-    k[:, :, m2, 0] = 20.0
+    k[:, :, m2, 0] = big
     k[:, :, m5] = k[:, :, m2]
-    k[:, :, m5[0], 0] = float(np.nextafter(np.float32(20.0), np.float32(np.inf)))
+    k[:, :, m5[0], 0] = float(np.nextafter(np.float32(big), np.float32(np.inf)))
     p, kmin, budget = 0.2, 1, ("none", 0.0)
     qn, kn = to_numpy(q), to_numpy(k)
     ref = routing.route(qn, kn, lay, p, kmin, budget)
