@@ -796,7 +796,7 @@ hipError_t launch_row_select(const Geo &g, double *SP, int32_t *order, int32_t *
     const int64_t R = (int64_t)g.BH * g.Nb;
     if (R == 0) return hipSuccess;
     const dim3 grid((unsigned)((R + kRowsPerGroup - 1) / kRowsPerGroup)), block(64 * kRowsPerGroup);
-    // the sort on the mass alone, then the exact sort of the rows it marked
+    // the sort on the truncated-mass keys, then the exact sort of the rows it marked
     for (int pass = 0; pass < 2; ++pass) {
         auto go = [&](auto fast, auto exact) {
             hipLaunchKernelGGL(pass == 0 ? fast : exact, grid, block, 0, s, g, SP, order, base, p, kmin);
