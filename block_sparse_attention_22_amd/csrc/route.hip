@@ -383,9 +383,12 @@ __device__ __forceinline__ void bitonic_keys(uint64_t *key, int lane, int e0) {
     }
 }
 
+constexpr int kIdxMask = 2047;     // index field of the sort key: rows of up to 2,048 slots
+
 template <int E, bool EXACT>
 __global__ __launch_bounds__(64 * kRowsPerGroup) void row_select_kernel(Geo g, double *SP, int32_t *order,
                                                                         int32_t *base, double p, int kmin) {
+    static_assert(64 * E <= kIdxMask + 1, "slot indices must fit the key's index field");
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kRowsPerGroup + (threadIdx.x >> 6);
     if (row >= (int64_t)g.BH * g.Nb) return;
@@ -420,25 +423,25 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void row_select_kernel(Geo g, d
     if (EXACT) {
         bitonic_row<E>(v, id, lane, e0);
     } else {
-        // Key = the high word of the mass's bit pattern (sign, exponent and
-        // 20 mantissa bits: order-preserving for masses >= 0, with no
-        // underflow) above the complemented index: one integer compare per
-        // exchange orders by (truncated mass desc, index asc).  The exact
-        // masses wait in LDS.  Two neighbours of the result that share a
-        // high word can still be out of exact order; a row with any such pair
-        // is left to the exact launch.
+        // Key = the mass's bit pattern with its low 11 bits replaced by the
+        // complemented index (entries < 64 * E <= 2048): the sign, exponent
+        // and 41 mantissa bits order masses >= 0 with no underflow, so one
+        // integer compare per exchange orders by (truncated mass desc, index
+        // asc).  The exact masses wait in LDS.  Two neighbours of the result
+        // whose masses agree above the low 11 bits can still be out of exact
+        // order; a row with any such pair is left to the exact launch.
         __shared__ double pl[kRowsPerGroup][64 * E];
         double *prow = pl[threadIdx.x >> 6];
         uint64_t key[E];
 #pragma unroll
         for (int r = 0; r < E; ++r) {
             prow[e0 + r] = v[r];
-            key[r] = ((uint64_t)__double2hiint(v[r]) << 32) | (uint32_t)~(uint32_t)(e0 + r);
+            key[r] = ((uint64_t)__double_as_longlong(v[r]) & ~(uint64_t)kIdxMask) | (uint32_t)(kIdxMask - (e0 + r));
         }
         bitonic_keys<E>(key, lane, e0);
 #pragma unroll
         for (int r = 0; r < E; ++r) {
-            id[r] = (int)~(uint32_t)key[r];
+            id[r] = kIdxMask - (int)((uint32_t)key[r] & kIdxMask);
             v[r] = (id[r] < Nk) ? prow[id[r]] : 0.0;
         }
         // Equal exact masses already sit in index order (the low word), so

@@ -173,28 +173,32 @@ def test_tied_masses_follow_block_order(dev, case):
 @pytest.mark.parametrize("grid,H,big", [((4, 16, 16), 2, 20.0), ((4, 160, 128), 1, 60.0)],
                          ids=["16_blocks", "1280_blocks"])
 def test_near_tied_masses_take_the_exact_order(dev, grid, H, big):
-    """Two masses that agree in their leading 20 mantissa bits but not below:
+    """Two masses that agree in all but the low 11 bits of their bit patterns:
     key block 5 is key block 2 with one coordinate of one token raised by one
-    float32 ulp, towards a query coordinate that is positive everywhere, so
-    block 5 holds the larger mass in every row by a relative 1e-8 or so.  The
-    routing sort's first pass orders on a truncated key, which puts the lower
-    index first; the exact order must win.  With p below the top mass and no
-    augmentation each row keeps exactly one block, so a misorder changes it.
-    16 blocks sort one slot per lane, 1,280 blocks 32 slots per lane."""
+    float32 ulp (1 -> 1 + 2^-23), along a query coordinate that is 3e-4
+    everywhere, so block 5 holds the larger mass in every row by a relative
+    5e-14 or so (far above fp64 rounding of the scores, below 2^-41).  The
+    routing sort's first pass orders on a key truncated to the high 53 bits,
+    which puts the lower index first in most rows; the exact order must win.
+    With p below the top mass and no augmentation each row keeps exactly one
+    block, so a misorder changes it.  16 blocks sort one slot per lane, 1,280
+    blocks 32 slots per lane."""
     tile = (1, 8, 8)                                   # blocks of 64 tokens
     q, k, v = _small_case(grid, tile, H, 128, "fp32", 90)
     lay = BlockLayout(grid, tile)
     m2, m5 = (torch.as_tensor(lay.members[j]) for j in (2, 5))
     q[..., 0] = q[..., 0].abs() + 1.0
+    q[..., 1] = 3e-4
     k[:, :, m2, 0] = big
+    k[:, :, m2, 1] = 1.0
     k[:, :, m5] = k[:, :, m2]
-    k[:, :, m5[0], 0] = float(np.nextafter(np.float32(big), np.float32(np.inf)))
+    k[:, :, m5[0], 1] = float(np.nextafter(np.float32(1.0), np.float32(2.0)))
     p, kmin, budget = 0.2, 1, ("none", 0.0)
     qn, kn = to_numpy(q), to_numpy(k)
     ref = routing.route(qn, kn, lay, p, kmin, budget)
     for hd in ref["heads"][0]:
         P = hd["P"]
-        assert np.all(P[:, 5] > P[:, 2]) and np.all(np.abs(P[:, 5] / P[:, 2] - 1) < 1e-7)
+        assert np.all(P[:, 5] > P[:, 2]) and np.all(np.abs(P[:, 5] / P[:, 2] - 1) < 1e-13)
         assert np.all(hd["base"] == 1)
     lists = fva.route(q.to(dev), k.to(dev), p, kmin, budget, grid=grid, tile=tile)
     g = gpu_lists_to_host(lists)
