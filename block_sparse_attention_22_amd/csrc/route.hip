@@ -385,8 +385,10 @@ __device__ __forceinline__ void bitonic_keys(uint64_t *key, int lane, int e0) {
 
 constexpr int kIdxMask = 2047;     // index field of the sort key: rows of up to 2,048 slots
 
+// The first launch asks for three waves per SIMD: at 32 slots per lane that
+// costs a few spilled registers and measured faster than two waves.
 template <int E, bool EXACT>
-__global__ __launch_bounds__(64 * kRowsPerGroup) void row_select_kernel(Geo g, double *SP, int32_t *order,
+__global__ __launch_bounds__(64 * kRowsPerGroup) __attribute__((amdgpu_waves_per_eu(EXACT ? 1 : 3))) void row_select_kernel(Geo g, double *SP, int32_t *order,
                                                                         int32_t *base, double p, int kmin) {
     static_assert(64 * E <= kIdxMask + 1, "slot indices must fit the key's index field");
     const int lane = threadIdx.x & 63;
@@ -427,22 +429,24 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) void row_select_kernel(Geo g, d
         // complemented index (entries < 64 * E <= 2048): the sign, exponent
         // and 41 mantissa bits order masses >= 0 with no underflow, so one
         // integer compare per exchange orders by (truncated mass desc, index
-        // asc).  The exact masses wait in LDS.  Two neighbours of the result
+        // asc).  The low 11 bits of each mass wait in LDS, so the exact mass
+        // is the key's high bits with them put back.  Two neighbours of the result
         // whose masses agree above the low 11 bits can still be out of exact
         // order; a row with any such pair is left to the exact launch.
-        __shared__ double pl[kRowsPerGroup][64 * E];
-        double *prow = pl[threadIdx.x >> 6];
+        __shared__ uint16_t pl[kRowsPerGroup][64 * E];
+        uint16_t *prow = pl[threadIdx.x >> 6];
         uint64_t key[E];
 #pragma unroll
         for (int r = 0; r < E; ++r) {
-            prow[e0 + r] = v[r];
-            key[r] = ((uint64_t)__double_as_longlong(v[r]) & ~(uint64_t)kIdxMask) | (uint32_t)(kIdxMask - (e0 + r));
+            const uint64_t bits = (uint64_t)__double_as_longlong(v[r]);
+            prow[e0 + r] = (uint16_t)(bits & kIdxMask);
+            key[r] = (bits & ~(uint64_t)kIdxMask) | (uint32_t)(kIdxMask - (e0 + r));
         }
         bitonic_keys<E>(key, lane, e0);
 #pragma unroll
         for (int r = 0; r < E; ++r) {
             id[r] = kIdxMask - (int)((uint32_t)key[r] & kIdxMask);
-            v[r] = (id[r] < Nk) ? prow[id[r]] : 0.0;
+            v[r] = __longlong_as_double((long long)((key[r] & ~(uint64_t)kIdxMask) | prow[id[r]]));
         }
         // Equal exact masses already sit in index order (the low word), so
         // the only misorder is a smaller mass before a larger one.
