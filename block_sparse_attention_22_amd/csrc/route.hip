@@ -598,9 +598,29 @@ __global__ __launch_bounds__(kAugThreads) void augment_kernel(Geo g, const doubl
         lo[q] = m[q];
         hi[q] = (q < nr) ? Nb : 0;
     }
-    uint64_t x = 0;
+    // Every candidate mass lies between the largest (the first entry of some
+    // row's tail) and the smallest (the last entry of some row), so all of
+    // them share the leading bits on which those two agree (bit patterns of
+    // masses >= 0 order like the masses).  The search starts at the 4-bit
+    // digit that holds their first difference, with x = the shared bits
+    // above it: the digits the rounds before it would have chosen.
+    __shared__ uint64_t ured[kAugThreads / 64];
+    uint64_t cmax = 0, cmin = ~0ull;
+#pragma unroll
+    for (int q = 0; q < kAugRows; ++q) {
+        if (q < nr && m[q] < Nb) {
+            const double *row = SP + ((int64_t)bh * Nb + r0 + q) * Nb;
+            cmax = max(cmax, double_bits(row[m[q]]));
+            cmin = min(cmin, double_bits(row[Nb - 1]));
+        }
+    }
+    cmax = block_reduce<kAugThreads>(cmax, ured, [](uint64_t a, uint64_t c) { return max(a, c); });
+    cmin = block_reduce<kAugThreads>(cmin, ured, [](uint64_t a, uint64_t c) { return min(a, c); });
+    const uint64_t diff = cmax ^ cmin;
+    const int sh0 = diff ? ((63 - __clzll((long long)diff)) & ~3) : 0;
+    uint64_t x = (sh0 >= 60) ? 0 : (cmax >> (sh0 + 4)) << (sh0 + 4);
     bool direct = false;
-    for (int sh = 60; sh >= 0; sh -= 4) {
+    for (int sh = sh0; sh >= 0; sh -= 4) {
         if (tid < 16) cnt[tid] = 0;
         __syncthreads();
         int pos[kAugRows][16];
