@@ -343,6 +343,21 @@ __device__ __forceinline__ void cross_stage_key(uint64_t *key, int lane, bool up
     }
 }
 
+// Descending compare-exchange of two keys read as doubles: a gets the larger,
+// b the smaller.  Keys are bit patterns of finite doubles >= 0 (fp64
+// denormals are kept), so the double order is the key order; a lane that
+// sorts ascending flips the sign bit of its keys first, which reverses the
+// order.  The instructions are written out because the library maximum
+// first canonicalises operands that it cannot prove are not NaN.
+__device__ __forceinline__ void key_maxmin(uint64_t &a, uint64_t &b) {
+    const double x = __longlong_as_double((long long)a), y = __longlong_as_double((long long)b);
+    double mx, mn;
+    asm("v_max_f64 %0, %1, %2" : "=v"(mx) : "v"(x), "v"(y));
+    asm("v_min_f64 %0, %1, %2" : "=v"(mn) : "v"(x), "v"(y));
+    a = (uint64_t)__double_as_longlong(mx);
+    b = (uint64_t)__double_as_longlong(mn);
+}
+
 template <int E>
 __device__ __forceinline__ void bitonic_keys(uint64_t *key, int lane, int e0) {
     constexpr int NKP = 64 * E;
@@ -353,10 +368,8 @@ __device__ __forceinline__ void bitonic_keys(uint64_t *key, int lane, int e0) {
 #pragma unroll
             for (int r = 0; r < E; ++r)
                 if (!(r & j)) {
-                    const uint64_t a = key[r], b = key[r + j];
-                    const bool sw = (b > a) == ((r & k) == 0);
-                    key[r] = sw ? b : a;
-                    key[r + j] = sw ? a : b;
+                    if ((r & k) == 0) key_maxmin(key[r], key[r + j]);
+                    else key_maxmin(key[r + j], key[r]);
                 }
     for (int k = E; k <= NKP; k <<= 1) {
         const bool up = (e0 & k) == 0;
@@ -370,16 +383,16 @@ __device__ __forceinline__ void bitonic_keys(uint64_t *key, int lane, int e0) {
                 default: cross_stage_key<32, E>(key, lane, up); break;
             }
         }
+        const uint64_t sgn = up ? 0 : (1ull << 63);
+#pragma unroll
+        for (int r = 0; r < E; ++r) key[r] ^= sgn;
 #pragma unroll
         for (int j = E / 2; j >= 1; j >>= 1)
 #pragma unroll
             for (int r = 0; r < E; ++r)
-                if (!(r & j)) {
-                    const uint64_t a = key[r], b = key[r + j];
-                    const bool sw = (b > a) == up;
-                    key[r] = sw ? b : a;
-                    key[r + j] = sw ? a : b;
-                }
+                if (!(r & j)) key_maxmin(key[r], key[r + j]);
+#pragma unroll
+        for (int r = 0; r < E; ++r) key[r] ^= sgn;
     }
 }
 
