@@ -208,6 +208,35 @@ def test_near_tied_masses_take_the_exact_order(dev, grid, H, big):
     assert np.all(np.diff(g["row_ptr"]) == 1) and np.all(g["col_idx"][: H * lay.Nb] == 5)
 
 
+def test_masses_down_to_denormals_and_zeros(dev):
+    """Routing masses spanning the whole fp64 range: every query block scores
+    key block j at -90 j, so its masses are e^(-90 j) / sum: normal down to
+    j = 7, a denormal at j = 8 (e^-720) and exact zeros beyond.  With p = 0.9,
+    a floor of 2 and a budget of 5x the base count, augmentation takes every
+    row's j = 2..8 and then 16 of the 112 equal zero masses, which go to the
+    lowest rows first (ties to lower (i, j)): rows 0 and 1 take all 7 of
+    theirs and row 2 takes 2."""
+    grid, tile, H = (4, 16, 16), (1, 8, 8), 1           # 16 blocks of 64 tokens
+    lay = BlockLayout(grid, tile)
+    N = grid[0] * grid[1] * grid[2]
+    q = torch.zeros((1, H, N, 128), dtype=torch.float32)
+    k = torch.zeros_like(q)
+    q[..., 0] = 1.0
+    for j in range(lay.Nb):
+        k[:, :, torch.as_tensor(lay.members[j]), 0] = -90.0 * j * np.sqrt(128.0)
+    p, kmin, budget = 0.9, 2, ("frac", 4.0)
+    ref = routing.route(to_numpy(q), to_numpy(k), lay, p, kmin, budget)
+    P = ref["heads"][0][0]["P"]
+    assert 0 < P[0, 8] < np.finfo(np.float64).tiny and np.all(P[:, 9:] == 0) and P[0, 7] >= np.finfo(np.float64).tiny
+    lists = fva.route(q.to(dev), k.to(dev), p, kmin, budget, grid=grid, tile=tile)
+    g = gpu_lists_to_host(lists)
+    rep = compare_lists(g, ref, p, budget, lay, 1, H)
+    print(f"\n[denormals] {rep}", flush=True)
+    assert rep["exact_rows"] == rep["rows"]
+    counts = np.diff(g["row_ptr"])
+    assert list(counts[:4]) == [16, 16, 11, 9] and np.all(counts[3:] == 9)
+
+
 def test_batch_and_strided_views(dev):
     grid, tile = (3, 16, 24), (2, 8, 8)
     q, k, v = _small_case(grid, tile, 3, 128, "bf16", 70, scale=2.0, B=2)

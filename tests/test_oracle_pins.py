@@ -349,3 +349,28 @@ def test_hilbert_layout_blocks(grid, nb, last):
     assert cube_bits(grid) == max(1, int(np.ceil(np.log2(max(grid)))))
     assert lay.Nb == nb and lay.sizes[-1] == last and (lay.sizes[:-1] == 128).all()
     assert np.array_equal(np.sort(np.concatenate(lay.members)), np.arange(lay.N))    # a partition
+
+
+def test_augmentation_ties_among_zero_masses_go_to_lower_rows():
+    """Hand-worked: 16 query blocks all score key block j at -90 j, so every
+    row's masses are e^(-90 j) / sum (normal to j = 7, denormal at j = 8,
+    exactly 0 beyond).  p = 0.9 with a floor of 2 keeps j = 0, 1 in every row
+    (K = 32); a budget of K + 4K adds A = 128 = 7 x 16 positive masses
+    (j = 2..8 of every row) plus 16 of the 112 equal zero masses, which go to
+    the lowest rows first, each row's in ascending j: rows 0 and 1 take 7,
+    row 2 takes 2."""
+    grid, tile = (4, 16, 16), (1, 8, 8)
+    lay = BlockLayout(grid, tile)
+    N = grid[0] * grid[1] * grid[2]
+    q = np.zeros((1, 1, N, 128))
+    k = np.zeros_like(q)
+    q[..., 0] = 1.0
+    for j in range(lay.Nb):
+        k[0, 0, lay.members[j], 0] = -90.0 * j * np.sqrt(128.0)
+    ref = routing.route(q, k, lay, 0.9, 2, ("frac", 4.0))
+    hd = ref["heads"][0][0]
+    assert np.all(hd["base"] == 2)
+    assert 0 < hd["P"][0, 8] < np.finfo(np.float64).tiny and np.all(hd["P"][:, 9:] == 0)
+    assert list(np.diff(ref["row_ptr"])) == [16, 16, 11] + [9] * 13
+    cols = ref["col_idx"]
+    assert list(cols[:16]) == list(range(16)) and list(cols[32:43]) == list(range(11))
