@@ -193,7 +193,7 @@ def main():
         with torch.cuda.stream(side):
             if ev:
                 ev[5].record()
-            fva.attn_prepare(kd, vd, **blk)
+            fva.attn_prepare(kd, vd, **blk, stream=main)
             if ev:
                 ev[6].record()
         if ev:

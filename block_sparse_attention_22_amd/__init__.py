@@ -62,7 +62,8 @@ FVA_ATTN_NO_ROW_PAIRS = 2
 class PlanInfo(ctypes.Structure):
     _fields_ = [("n_items", ctypes.c_int32), ("chunk_blocks", ctypes.c_int32), ("n_split_rows", ctypes.c_int32),
                 ("n_partials", ctypes.c_int32), ("total_blocks", ctypes.c_int64), ("num_ctas", ctypes.c_int32),
-                ("n_row_pairs", ctypes.c_int32)]
+                ("n_row_pairs", ctypes.c_int32), ("kept_pairs", ctypes.c_int64),
+                ("predicted_imbalance", ctypes.c_float), ("reserved", ctypes.c_int32)]
 
 
 class CtaStat(ctypes.Structure):
@@ -70,7 +71,7 @@ class CtaStat(ctypes.Structure):
                 ("blocks", ctypes.c_uint32), ("t_start", ctypes.c_uint64), ("t_end", ctypes.c_uint64)]
 
 
-EXPORTS = ("fva_num_blocks", "fva_hilbert_order", "fva_lists_capacity", "fva_route_workspace_bytes", "fva_route",
+EXPORTS = ("fva_num_blocks", "fva_block_sizes", "fva_hilbert_order", "fva_lists_capacity", "fva_route_workspace_bytes", "fva_route",
            "fva_attn_workspace_bytes", "fva_attn_stats_bytes", "fva_attn_prepare", "fva_sparse_attn",
            "fva_status_string")
 
@@ -96,6 +97,8 @@ def load_library(path: Optional[str] = None):
         lib = ctypes.CDLL(p)
         P = ctypes.POINTER
         lib.fva_num_blocks.argtypes = [P(Problem), P(ctypes.c_int32), P(ctypes.c_int32)]
+        lib.fva_block_sizes.argtypes = [P(Problem), P(ctypes.c_int32)]
+        lib.fva_block_sizes.restype = ctypes.c_int
         lib.fva_hilbert_order.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P(ctypes.c_int32)]
         lib.fva_hilbert_order.restype = ctypes.c_int
         lib.fva_num_blocks.restype = ctypes.c_int
@@ -188,30 +191,34 @@ def hilbert_order(grid, device=None) -> torch.Tensor:
     return t
 
 
+def _shape_problem(grid, tile, ordered, B=1, H=1, d=128, dtype=torch.bfloat16) -> Problem:
+    """A problem descriptor that carries only a shape (the calls that take it
+    compute counts and never touch device memory)."""
+    T, Y, X = (int(a) for a in grid)
+    return Problem(B, H, d, T, Y, X, *(tile if tile is not None else (1, 1, 1)),
+                   FVA_BF16 if dtype == torch.bfloat16 else FVA_F32, H * T * Y * X * d, T * Y * X * d, d,
+                   256 if ordered else None)      # any aligned non-null address stands for a token order
+
+
 def block_sizes(grid, tile, ordered: bool = False):
-    """Valid tokens of every block: tile raster order (edge tiles hold fewer),
-    or, ``ordered``, 128-token runs of a token order (the last holds the rest)."""
+    """Valid tokens of every block (fva_block_sizes): tile raster order (edge
+    tiles hold fewer), or, ``ordered``, 128-token runs of a token order."""
     import numpy as np
-    if ordered:
-        N = int(grid[0]) * int(grid[1]) * int(grid[2])
-        nb = -(-N // 128)
-        sz = np.full(nb, 128, dtype=np.int64)
-        sz[-1] = N - 128 * (nb - 1)
-        return sz
-    ext = []
-    for g, t in zip(grid, tile):
-        n = -(-int(g) // int(t))
-        e = np.full(n, int(t), dtype=np.int64)
-        e[-1] = int(g) - (n - 1) * int(t)
-        ext.append(e)
-    return (ext[0][:, None, None] * ext[1][None, :, None] * ext[2][None, None, :]).reshape(-1)
+    p = _shape_problem(grid, tile, ordered)
+    nq = ctypes.c_int32()
+    lib = load_library()
+    st = lib.fva_num_blocks(ctypes.byref(p), ctypes.byref(nq), ctypes.byref(ctypes.c_int32()))
+    if st != FVA_OK:
+        raise FvaError(st, "fva_num_blocks")
+    out = np.empty(nq.value, dtype=np.int32)
+    st = lib.fva_block_sizes(ctypes.byref(p), out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    if st != FVA_OK:
+        raise FvaError(st, "fva_block_sizes")
+    return out.astype(np.int64)
 
 
 def num_blocks(grid, tile, *, B=1, H=1, d=128, dtype=torch.bfloat16, ordered: bool = False) -> int:
-    T, Y, X = grid
-    p = Problem(B, H, d, T, Y, X, *(tile if tile is not None else (1, 1, 1)),
-                FVA_BF16 if dtype == torch.bfloat16 else FVA_F32, H * T * Y * X * d, T * Y * X * d, d,
-                256 if ordered else None)      # any aligned non-null address: only the count is computed
+    p = _shape_problem(grid, tile, ordered, B, H, d, dtype)
     nq, nk = ctypes.c_int32(), ctypes.c_int32()
     st = load_library().fva_num_blocks(ctypes.byref(p), ctypes.byref(nq), ctypes.byref(nk))
     if st != FVA_OK:
@@ -219,17 +226,29 @@ def num_blocks(grid, tile, *, B=1, H=1, d=128, dtype=torch.bfloat16, ordered: bo
     return nq.value
 
 
-# Workspaces are plain device byte buffers owned here and reused between calls.
+# Workspaces are plain device byte buffers owned here, one per (kind of
+# call, device, stream), reused between calls and grown on demand.  Calls on
+# one stream run in order, so they can share one; calls on different streams
+# get different buffers and never race.  A buffer is allocated while its own
+# stream is current, so when it is replaced the caching allocator hands its
+# memory to other work only in that stream's order.
 _ws_cache = {}
 
 
-def _workspace(nbytes: int, device, key: str) -> torch.Tensor:
-    k = (key, device.index if device.index is not None else torch.cuda.current_device())
+def _workspace(nbytes: int, device, key: str, stream=None) -> torch.Tensor:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    k = (key, device.index if device.index is not None else torch.cuda.current_device(), s.cuda_stream)
     buf = _ws_cache.get(k)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(s):
+            buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _ws_cache[k] = buf
     return buf
+
+
+def release_workspaces() -> None:
+    """Drop every cached workspace (each is freed in its own stream's order)."""
+    _ws_cache.clear()
 
 
 def _stream(device) -> int:
@@ -270,7 +289,9 @@ def _budget(budget) -> Budget:
 def route(q: torch.Tensor, k: torch.Tensor, p: float, kmin: int, budget=None, *, grid, tile=None,
           order: Optional[torch.Tensor] = None,
           want_mask: bool = False, out: Optional[BlockLists] = None) -> BlockLists:
-    """Sparse-routing front end (fva_route): per-head CSR block lists."""
+    """Sparse-routing front end (fva_route): per-head CSR block lists.
+
+    Runs on the current stream with that stream's routing workspace."""
     _check_device_tensor("q", q)
     _check_device_tensor("k", k)
     if q.shape != k.shape or q.dtype != k.dtype or q.stride() != k.stride():
@@ -343,12 +364,13 @@ def _check_qkv(q, k, v):
 
 
 def attn_prepare(k: torch.Tensor, v: torch.Tensor, *, grid, tile=None, chunk_blocks: int = 0,
-                 num_ctas: int = 0, order: Optional[torch.Tensor] = None) -> None:
-    """The list-independent part of sparse_attn (fva_attn_prepare) on the
-    current stream, into the attention workspace that the next
-    ``sparse_attn(..., prepared=True)`` on this device uses with the same
-    k, v and options.  The caller orders the two (and this call after any
-    earlier sparse_attn still reading the workspace), e.g. with
+                 num_ctas: int = 0, order: Optional[torch.Tensor] = None, stream=None) -> None:
+    """The list-independent part of sparse_attn (fva_attn_prepare), enqueued
+    on the current stream, into the attention workspace of ``stream`` (the
+    stream on which the matching ``sparse_attn(..., prepared=True)`` with the
+    same k, v and options will run; default: the current stream).  The
+    caller orders the two (and this call after any earlier sparse_attn on
+    ``stream`` still reading that workspace), e.g. with
     ``Stream.wait_stream``."""
     _check_qkv(k, k, v)
     lib = load_library()
@@ -357,9 +379,12 @@ def attn_prepare(k: torch.Tensor, v: torch.Tensor, *, grid, tile=None, chunk_blo
     wsb = lib.fva_attn_workspace_bytes(ctypes.byref(prob), ctypes.byref(opts))
     if wsb == 0:
         raise FvaError(FVA_ERR_INVALID_ARG, "fva_attn_workspace_bytes")
-    ws = _workspace(wsb, k.device, "attn")
+    cur = torch.cuda.current_stream(k.device)
+    ws = _workspace(wsb, k.device, "attn", stream)
+    if stream is not None and stream.cuda_stream != cur.cuda_stream:
+        ws.record_stream(cur)     # the copies are written on this stream
     st = lib.fva_attn_prepare(ctypes.byref(prob), k.data_ptr(), v.data_ptr(), ws.data_ptr(), ws.numel(),
-                              ctypes.byref(opts), _stream(k.device))
+                              ctypes.byref(opts), cur.cuda_stream)
     if st != FVA_OK:
         raise FvaError(st, "fva_attn_prepare")
 
@@ -374,8 +399,9 @@ def sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lists: BlockL
     receives the plan header and per-workgroup timing records.
     ``kernel_events``: optional pair of timing-enabled torch.cuda.Event (or raw
     hipEvent_t ints) recorded right before and after the attention kernel.
-    ``prepared``: ``attn_prepare(k, v, ...)`` already ran (ordered before
-    this call) with the same tensors and options.
+    ``prepared``: ``attn_prepare(k, v, ..., stream=<this call's stream>)``
+    already ran (ordered before this call) with the same tensors and options.
+    Runs on the current stream with that stream's attention workspace.
     ``row_pairs``: let neighbouring query blocks of at most 64 tokens share a
     work item (bf16, head_dim 128; off: FVA_ATTN_NO_ROW_PAIRS).
     """
@@ -449,4 +475,4 @@ def per_cu_imbalance(ctas, num_cus: int):
 
 
 __all__ = ["route", "sparse_attn", "BlockLists", "make_problem", "num_blocks", "block_sizes", "load_library", "FvaError",
-           "stats_bytes", "parse_stats", "attn_prepare", "FVA_ATTN_PREPARED", "hilbert_order", "per_cu_imbalance", "lists_from_csr", "EXPORTS", "LIB_PATH"]
+           "stats_bytes", "parse_stats", "attn_prepare", "release_workspaces", "FVA_ATTN_PREPARED", "hilbert_order", "per_cu_imbalance", "lists_from_csr", "EXPORTS", "LIB_PATH"]

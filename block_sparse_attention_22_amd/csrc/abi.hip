@@ -261,6 +261,22 @@ fva_status fva_hilbert_order(int32_t grid_t, int32_t grid_y, int32_t grid_x, int
     return FVA_OK;
 }
 
+fva_status fva_block_sizes(const fva_problem *prob, int32_t *sizes) {
+    Geo g;
+    const fva_status st = make_geo(prob, &g);
+    if (st != FVA_OK) return st;
+    if (!sizes) return FVA_ERR_INVALID_ARG;
+    for (int j = 0; j < g.Nb; ++j) {
+        if (g.order) {
+            sizes[j] = std::min(kMaxSlots, g.N - j * kMaxSlots);
+            continue;
+        }
+        const int it = j / (g.nY * g.nX), iy = (j / g.nX) % g.nY, ix = j % g.nX;
+        sizes[j] = std::min(g.tt, g.T - it * g.tt) * std::min(g.ty, g.Y - iy * g.ty) * std::min(g.tx, g.X - ix * g.tx);
+    }
+    return FVA_OK;
+}
+
 size_t fva_lists_capacity(const fva_problem *prob) {
     Geo g;
     if (make_geo(prob, &g) != FVA_OK) return 0;
@@ -358,6 +374,7 @@ fva_status fva_sparse_attn(const fva_problem *prob, const void *q, const void *k
     FVA_TRY_HIP(launch_row_pairs(g, bsize, lists->row_ptr, lists->col_idx, rp, s));
     FVA_TRY_HIP(launch_plan(g, lists->row_ptr, chunk, sz.num_ctas, sz.cap_items, sz.cap_parts, rp, hdr, items, splits,
                             s));
+    if (stats) FVA_TRY_HIP(launch_plan_stats(g, lists->row_ptr, lists->col_idx, bsize, sz.num_ctas, items, hdr, s));
     hipEvent_t ev0 = opts ? (hipEvent_t)opts->kernel_events[0] : nullptr;
     hipEvent_t ev1 = opts ? (hipEvent_t)opts->kernel_events[1] : nullptr;
     FVA_TRY_HIP(launch_attention(g, q, k, v, o, lists->row_ptr, lists->col_idx, rp.ucol, tok, bsize, hdr, items,

@@ -273,9 +273,10 @@ __device__ __forceinline__ void compute_tile(const uint16_t *Kt, const uint16_t 
         for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[t][8 * hf + e], c, -mc));
-                l_run += pv;
-                pf[2 * t + hf][e] = (__bf16)pv;
+                // the denominator sums the bf16-rounded weights that P V uses
+                const __bf16 pb = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[t][8 * hf + e], c, -mc));
+                l_run += (float)pb;
+                pf[2 * t + hf][e] = pb;
             }
         }
     }
@@ -424,13 +425,48 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
 // LDS-DMA buffer loads issued one half block ahead from the block-major K and
 // V^T copies that pack_kv_kernel writes (every DMA address is a per-lane
 // constant plus a wave-uniform block offset, with no per-lane index loads).
-// Work items come from per-XCD queues (next_item_xcd).  The running row max
-// is only raised when it grows by more than 8 (log2 units), which skips most
-// rescales of the accumulator and keeps probabilities below 2^8 (exact: the
-// same offset is used in numerator and denominator).
+// Work items come from per-XCD queues (next_item_xcd).  The softmax offset
+// of a row (log2 units) is lazy: a half block's probabilities are first
+// formed against the current offset, and only when one of them could exceed
+// 2^16 (a lane's sum of them does; always true on an item's first half,
+// where the offset is -inf) is the offset raised to the exact running max,
+// the accumulator rescaled and the half recomputed.  The row max is thus
+// computed on a few halves per row instead of on every half, and no
+// probability exceeds 2^16.  Any offset is exact, since numerator and
+// denominator use the same one; the denominator sums the bf16-rounded
+// probabilities that P V uses, so that the two see identical weights.
 constexpr int kHalf = 64;                        // keys per half block
 constexpr int kHalfBytes = kHalf * 128 * 2;      // 16 KB: K or V^T of one half block
-constexpr float kLazyMax = 8.0f;
+constexpr float kLazyBound = 65536.0f;           // largest probability the fast path admits
+
+// Lane l and lane l ^ 32 (the two halves of one query's keys) combined by a
+// commutative operation, so both lanes get the same bits.
+__device__ __forceinline__ float max_halves(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
+__device__ __forceinline__ float sum_halves(float x) { return x + __shfl_xor(x, 32, 64); }
+
+// Probabilities of one wave's 64-key half block against the offset m:
+// p = exp2(s * c - m), rounded to bf16 into the B operands of P V; returns
+// this lane's sum of the ROUNDED values (v_dot2 with a pair of ones, two
+// partial sums).
+__device__ __forceinline__ float half_probs(const f32x16 *sacc, float c, float m, bf16x8 *pf) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const float a = __builtin_amdgcn_exp2f(fmaf(sacc[t][8 * hf + e], c, -m));
+                const float b = __builtin_amdgcn_exp2f(fmaf(sacc[t][8 * hf + e + 1], c, -m));
+                const bf16x2 pr = {(__bf16)a, (__bf16)b};
+                pf[2 * t + hf][e] = pr[0];
+                pf[2 * t + hf][e + 1] = pr[1];
+                if (hf == 0) s0 = __builtin_amdgcn_fdot2_f32_bf16(pr, one, s0, false);
+                else s1 = __builtin_amdgcn_fdot2_f32_bf16(pr, one, s1, false);
+            }
+    return s0 + s1;
+}
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
@@ -571,13 +607,19 @@ __device__ __forceinline__ void half_tile(const uint16_t *Kt, const uint16_t *Vt
             for (int r = 0; r < 16; ++r)
                 if (32 * t + 16 * (r >> 3) + (r & 7) >= lim) sacc[t][r] = -INFINITY;
     }
-    float mloc = -INFINITY;
+    bf16x8 pf[4];
+    float hs = half_probs(sacc, c, m_run, pf);
+    // Slow path (wave-uniform): some lane's probabilities may exceed the
+    // bound, or are not numbers (the offset was -inf, or a masked key met an
+    // infinite offset): raise the offset to the exact running max and redo
+    // the half.  Afterwards every probability is at most 1.
+    if (__any(!(hs <= kLazyBound))) {
+        float mloc = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[t][r]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * c;
-    if (__any(mloc > m_run + kLazyMax)) {
+            for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[t][r]);
+        mloc = max_halves(mloc) * c;
         const float mnew = fmaxf(m_run, mloc);
         const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
         m_run = mnew;
@@ -586,18 +628,9 @@ __device__ __forceinline__ void half_tile(const uint16_t *Kt, const uint16_t *Vt
         for (int u = 0; u < 4; ++u)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[u][r] *= alpha;
+        hs = half_probs(sacc, c, m_run, pf);
     }
-    bf16x8 pf[4];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[t][8 * hf + e], c, -m_run));
-                l_run += pv;
-                pf[2 * t + hf][e] = (__bf16)pv;
-            }
+    l_run += hs;
 #pragma unroll
     for (int sg = 0; sg < 4; ++sg) {
         bf16x8 vf[4];
@@ -728,7 +761,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
             __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): the last (reload) DMA has landed
             __syncthreads();       // all waves done with both stages before the next item's DMA
         }
-        const float l = l_run + __shfl_xor(l_run, 32, 64);
+        const float l = sum_halves(l_run);
         if (active && qvalid) {
             if (part < 0) {
                 const float inv = (l > 0.f) ? 1.f / l : 0.f;
@@ -1162,7 +1195,77 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int R, int Nb, const
         hdr->info.total_blocks = total;
         hdr->info.num_ctas = num_ctas;
         hdr->info.n_row_pairs = n_pairs;
+        hdr->info.kept_pairs = 0;
+        hdr->info.predicted_imbalance = 0.f;
+        hdr->info.reserved = 0;
         for (int q = 0; q < 8; ++q) hdr->queue[q] = 0;
+    }
+}
+
+// ----------------------------------------------------------- plan stats
+// Only when the caller asks for stats.  One wave per row: n_i times the sum
+// of n_j over the row's kept blocks, added into the plan header.
+__global__ __launch_bounds__(256) void kept_pairs_kernel(int R, int Nb, const int32_t *row_ptr, const int32_t *col_idx,
+                                                         const int32_t *bsize, PlanHeader *hdr) {
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= R) return;
+    const int b0 = row_ptr[r], b1 = row_ptr[r + 1];
+    long long s = 0;
+    for (int e = b0 + lane; e < b1; e += 64) s += bsize[col_idx[e]];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    if (lane == 0 && s != 0)
+        atomicAdd(reinterpret_cast<unsigned long long *>(&hdr->info.kept_pairs),
+                  (unsigned long long)(s * bsize[r % Nb]));
+}
+
+// One wave: the items in queue order, each to the workgroup with the least
+// work so far (ties to the lower index), cost = the item's key blocks; the
+// loads stay in registers (kMaxPredict / 64 per lane) and each step is an
+// argmin over the wave.  Writes max load / mean load.
+constexpr int kMaxPredict = 1024;   // workgroups the prediction handles (16 loads per lane)
+__global__ __launch_bounds__(64) void predict_kernel(int num_ctas, const WorkItem *items, PlanHeader *hdr) {
+    constexpr int PER = kMaxPredict / 64;
+    const int lane = threadIdx.x;
+    const int n_items = hdr->info.n_items;
+    float load[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) load[u] = (u * 64 + lane < num_ctas) ? 0.f : INFINITY;
+    double total = 0.0;
+    for (int it = 0; it < n_items; ++it) {
+        const WorkItem wi = items[it];
+        const float cost = (float)(wi.kb_end - wi.kb_begin);
+        total += cost;
+        float best = load[0];
+        int bi = 0;
+#pragma unroll
+        for (int u = 1; u < PER; ++u) {
+            const bool lt = load[u] < best;
+            best = lt ? load[u] : best;
+            bi = lt ? u : bi;
+        }
+        int widx = bi * 64 + lane;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const float ob = __shfl_xor(best, o, 64);
+            const int ow = __shfl_xor(widx, o, 64);
+            const bool take = (ob < best) || (ob == best && ow < widx);
+            best = take ? ob : best;
+            widx = take ? ow : widx;
+        }
+#pragma unroll
+        for (int u = 0; u < PER; ++u)
+            if (u * 64 + lane == widx) load[u] += cost;
+    }
+    float mx = 0.f;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) mx = (u * 64 + lane < num_ctas) ? fmaxf(mx, load[u]) : mx;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if (lane == 0) {
+        const double mean = total / num_ctas;
+        hdr->info.predicted_imbalance = mean > 0.0 ? (float)(mx / mean) : 1.f;
     }
 }
 
@@ -1228,6 +1331,16 @@ hipError_t launch_plan(const Geo &g, const int32_t *row_ptr, int chunk_mode, int
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, g.BH * g.Nb, g.Nb, row_ptr, chunk_mode, num_ctas,
                        cap_items, cap_parts, pairs ? rp.role : nullptr, pairs ? rp.ulen : nullptr, rp.max_pairs, hdr,
                        items, splits);
+    return hipGetLastError();
+}
+
+hipError_t launch_plan_stats(const Geo &g, const int32_t *row_ptr, const int32_t *col_idx, const int32_t *bsize,
+                             int num_ctas, const WorkItem *items, PlanHeader *hdr, hipStream_t s) {
+    const int R = g.BH * g.Nb;
+    if (R > 0)
+        hipLaunchKernelGGL(kept_pairs_kernel, dim3((R + 3) / 4), dim3(256), 0, s, R, g.Nb, row_ptr, col_idx, bsize,
+                           hdr);
+    if (num_ctas <= kMaxPredict) hipLaunchKernelGGL(predict_kernel, dim3(1), dim3(64), 0, s, num_ctas, items, hdr);
     return hipGetLastError();
 }
 

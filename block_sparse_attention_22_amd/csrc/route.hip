@@ -453,6 +453,23 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) __attribute__((amdgpu_waves_per
         sum += ex;
     }
     sum = wave_sum(sum);
+    int32_t *orow = order + row * Nk;
+    if (!isfinite(sum)) {
+        // A score that is not a finite number (from a non-finite q or k
+        // token) leaves the row's masses undefined, so no prefix reaches p:
+        // the row keeps every key block, in block order, and offers no
+        // augmentation candidate.  The sort never sees such a row (a NaN
+        // key would break the network's permutation).  Wave-uniform.
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+            if (e0 + r < Nk) {
+                srow[e0 + r] = 0.0;
+                orow[e0 + r] = e0 + r;
+            }
+        }
+        if (lane == 0) base[row] = Nk;
+        return;
+    }
 #pragma unroll
     for (int r = 0; r < E; ++r) v[r] = (e0 + r < Nk) ? v[r] / sum : 0.0;   // padding: +0, index >= Nk
 
@@ -517,7 +534,6 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) __attribute__((amdgpu_waves_per
     const int m_p = (p >= 1.0) ? Nk : first;
     const int m = min(Nk, max(m_p, kmin));
 
-    int32_t *orow = order + row * Nk;
 #pragma unroll
     for (int r = 0; r < E; ++r) {
         if (e0 + r < Nk) {
@@ -807,7 +823,7 @@ __global__ __launch_bounds__(64) void csr_kernel(Geo g, const int32_t *order, co
     const int32_t *ord = order + row * Nk;
     for (int r = lane; r < cnt; r += 64) {
         const int j = ord[r];
-        atomicOr(&bits[j >> 5], 1u << (j & 31));
+        if ((unsigned)j < (unsigned)Nk) atomicOr(&bits[j >> 5], 1u << (j & 31));
     }
     __syncthreads();
     const uint32_t word = (lane < W) ? bits[lane] : 0u;

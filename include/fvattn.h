@@ -157,6 +157,16 @@ typedef struct {
     int64_t total_blocks;  /* kept (query block, key block) pairs */
     int32_t num_ctas;      /* persistent workgroups launched */
     int32_t n_row_pairs;   /* work items that ran two query blocks together */
+    /* Kept valid token pairs: the sum over kept (query block i, key block j)
+     * of n_i * n_j, with n the blocks' token counts.  4 * head_dim times this
+     * is the attention's useful flop count. */
+    int64_t kept_pairs;
+    /* The plan's predicted load balance: the work items, in queue order, each
+     * given to the workgroup with the least work so far (ties to the lower
+     * workgroup), cost = key blocks of the item; the largest workgroup load
+     * over the mean (0 when more than 1,024 workgroups run). */
+    float predicted_imbalance;
+    int32_t reserved;      /* 0 */
 } fva_plan_info;
 
 typedef struct {
@@ -185,6 +195,13 @@ fva_status fva_hilbert_order(int32_t grid_t, int32_t grid_y, int32_t grid_x, int
  * invalid or unsupported problem. */
 fva_status fva_num_blocks(const fva_problem *prob, int32_t *nq, int32_t *nk);
 
+/* Host only: the valid token count of every block (the block organisation
+ * of `prob`: tile extents clipped at the grid's far edges, or 128-token runs
+ * of the token order with the remainder in the last), in block order.
+ * sizes: host int32 [Nq].  prob->token_order is only tested against NULL.
+ * FVA_ERR_* on an invalid or unsupported problem or a NULL sizes. */
+fva_status fva_block_sizes(const fva_problem *prob, int32_t *sizes);
+
 /* col_idx capacity in entries: batch*heads*Nq*Nk (0 if the problem is invalid). */
 size_t fva_lists_capacity(const fva_problem *prob);
 
@@ -207,7 +224,9 @@ fva_status fva_route(const fva_problem *prob, const void *q, const void *k, doub
 size_t fva_attn_workspace_bytes(const fva_problem *prob, const fva_attn_options *opts);
 
 /* Bytes of the stats buffer: one fva_plan_info then one fva_cta_stat per
- * persistent workgroup (0 if the problem or options are invalid). */
+ * persistent workgroup (0 if the problem or options are invalid).  Passing a
+ * stats buffer adds two small launches before the attention kernel (the
+ * pair count and the plan's load prediction). */
 size_t fva_attn_stats_bytes(const fva_problem *prob, const fva_attn_options *opts);
 
 /*

@@ -56,11 +56,6 @@ def sparse_attention_head(q, k, v, layout: BlockLayout, row_ptr, col_idx,
     return o
 
 
-def dense_attention_head(q, k, v, precision: str = "fp64"):
-    """Plain softmax attention over all tokens (the p = 1 special case)."""
-    return _rows_softmax_av(q, k, v, precision)
-
-
 def kept_pairs(layout: BlockLayout, row_ptr, col_idx, nrows_per_head: int):
     """Kept valid query-key token pairs: sum over kept (i, j) of n_i * n_j.
 

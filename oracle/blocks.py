@@ -48,9 +48,3 @@ class BlockLayout:
     def padded_N(self) -> int:
         """Tokens after padding every axis up to a tile multiple."""
         return self.nT * self.tt * self.nY * self.ty * self.nX * self.tx
-
-    def block_of_token(self) -> np.ndarray:
-        owner = np.full(self.N, -1, dtype=np.int64)
-        for b, m in enumerate(self.members):
-            owner[m] = b
-        return owner

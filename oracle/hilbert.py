@@ -110,9 +110,3 @@ class HilbertLayout:
     @property
     def padded_N(self) -> int:
         return self.Nb * self.block
-
-    def block_of_token(self) -> np.ndarray:
-        owner = np.empty(self.N, dtype=np.int64)
-        for b, m in enumerate(self.members):
-            owner[m] = b
-        return owner

@@ -58,7 +58,9 @@ def row_softmax(s: np.ndarray) -> np.ndarray:
 def importance_order(P: np.ndarray) -> np.ndarray:
     """O4: per row, key-block indices by P descending; equal P -> lower j first.
 
-    A stable sort of -P keeps equal keys in ascending j.
+    A stable sort of -P keeps equal keys in ascending j.  A row whose masses
+    are all NaN (the softmax of a row holding a non-finite score) stays in
+    block order.
     """
     return np.argsort(-P, axis=1, kind="stable")
 
@@ -79,6 +81,10 @@ def topp_floor(P: np.ndarray, order: np.ndarray, p: float, kmin: int):
         reached = c >= p
         m_p = np.where(reached.any(axis=1), reached.argmax(axis=1) + 1, Nk)
     m = np.minimum(Nk, np.maximum(m_p, int(kmin)))
+    # A row whose masses are not finite numbers (a non-finite q or k token
+    # upstream) has no prefix whose mass reaches p, so it keeps every block;
+    # importance_order leaves such a row in block order.
+    assert np.all(m[~np.isfinite(P).all(axis=1)] == Nk)
     return m.astype(np.int64), c
 
 
@@ -191,9 +197,3 @@ def route(q, k, layout: BlockLayout, p: float, kmin: int, budget=("none", 0.0), 
     return dict(heads=heads, base=base, count=count, row_ptr=row_ptr, col_idx=col_idx,
                 head_kept=np.asarray(kept, dtype=np.int64), Nq=Nq, Nk=Nk)
 
-
-def augment_from_base(P, order, base, budget_total):
-    """O6 recomputed from given base counts (used to check a GPU's augmentation
-    given that GPU's own base counts): returns add[i]."""
-    A = int(budget_total - int(np.sum(base)))
-    return augment(P, order, np.asarray(base, dtype=np.int64), A)

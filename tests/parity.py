@@ -2,9 +2,12 @@
 outputs with the CPU oracle.
 
 List rule: bit-exact, except that a row's Top-p count may differ where the
-oracle's cumulative mass lies within 1e-5 of p, and masses within 1e-12 of
-each other may swap (float64 summation order); augmentation is re-derived by
-the oracle from the GPU's own base counts so one excused row cannot cascade.
+oracle's cumulative mass lies within 1e-5 of p, and two masses that agree to
+a relative 1e-12 may swap at a cut (the two sides sum the float64 pooled
+means and scores in different orders, which moves a mass by ~1e-16 of
+itself); augmentation is re-derived by the oracle from the GPU's own base
+counts so one excused row cannot cascade.  Every use of either excuse is
+counted; the workload tests require both counts to be zero.
 Output rule: max |o_gpu - o_oracle| over the checked rows, the oracle run on
 the GPU's own lists, in float64 (float32 products for the large layers).
 """
@@ -16,7 +19,7 @@ import torch
 from oracle import BlockLayout, attention, routing
 
 P_WINDOW = 1e-5
-TIE_EPS = 1e-12
+TIE_REL = 1e-12   # relative: |P_a - P_b| <= TIE_REL * max(P_a, P_b)
 
 
 def to_numpy(t: torch.Tensor, dtype=np.float64) -> np.ndarray:
@@ -73,10 +76,16 @@ def compare_lists(gpu: dict, ref: dict, p: float, budget, layout: BlockLayout, B
                 diff = np.setxor1d(got, exp)
                 P = hd["P"][i]
                 bnd = [P[exp].min()] + ([tau] if tau is not None else [])
-                ok = all(any(abs(P[x] - t) <= TIE_EPS for t in bnd) for x in diff)
+                ok = all(any(abs(P[x] - t) <= TIE_REL * max(P[x], t) for t in bnd) for x in diff)
                 assert ok, f"head {bh} row {i}: lists differ beyond near-ties: gpu {got} oracle {exp}"
                 rep["excused_tie_rows"] += 1
     return rep
+
+
+def assert_exact(rep: dict) -> None:
+    """Every row matched the oracle without either excuse."""
+    assert rep["excused_count_rows"] == 0 and rep["excused_tie_rows"] == 0, rep
+    assert rep["exact_rows"] == rep["rows"], rep
 
 
 def head_csr(rp, ci, bh, Nb):

@@ -43,6 +43,21 @@ def prob(**kw):
     return Problem(**base)
 
 
+@pytest.mark.parametrize("grid,tile", [((21, 45, 80), (2, 8, 8)), ((21, 68, 120), (2, 8, 8)), ((5, 30, 52), (2, 8, 8)),
+                                       ((4, 8, 8), (1, 8, 8)), ((1, 5, 5), (2, 8, 8)), ((5, 9, 11), (1, 3, 5)),
+                                       ((21, 45, 80), None), ((5, 20, 20), None), ((1, 5, 5), None)])
+def test_block_sizes_match_the_oracle_layout(lib, grid, tile):
+    """fva_block_sizes (the library's block organisation, on the host) against
+    the oracle's own layouts: tile blocks and Hilbert-curve 128-token runs."""
+    import numpy as np
+    from oracle import BlockLayout, HilbertLayout
+    lay = BlockLayout(grid, tile) if tile is not None else HilbertLayout(grid)
+    got = fva.block_sizes(grid, tile, ordered=tile is None)
+    assert np.array_equal(got, lay.sizes)
+    p = prob(grid_t=grid[0], grid_y=grid[1], grid_x=grid[2])
+    assert lib.fva_block_sizes(ctypes.byref(p), None) == FVA_ERR_INVALID_ARG
+
+
 def nblocks(lib, p):
     nq, nk = ctypes.c_int32(), ctypes.c_int32()
     st = lib.fva_num_blocks(ctypes.byref(p), ctypes.byref(nq), ctypes.byref(nk))

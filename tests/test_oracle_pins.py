@@ -302,6 +302,29 @@ def test_kept_pairs_counts_valid_tokens():
     assert per_head.tolist() == [tot]
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_kept_pairs_by_token_enumeration(seed):
+    """Brute force: count every (query token, key token) pair whose key's
+    block is kept by the query's block, over ragged tiles and two heads."""
+    lay = BlockLayout((3, 5, 7), (2, 2, 4))          # 2 x 3 x 2 = 12 blocks of 16, 8, 4, 12, 6, 3 tokens
+    rng = np.random.default_rng(40 + seed)
+    H = 2
+    rows = []
+    for _ in range(H * lay.Nb):
+        rows.append(np.sort(rng.choice(lay.Nb, rng.integers(0, lay.Nb + 1), replace=False)))
+    rp = np.concatenate([[0], np.cumsum([len(r) for r in rows])])
+    ci = np.concatenate(rows)
+    owner = np.empty(lay.N, dtype=np.int64)
+    for b, m in enumerate(lay.members):
+        owner[m] = b
+    expect = []
+    for h in range(H):
+        kept = [set(rows[h * lay.Nb + i].tolist()) for i in range(lay.Nb)]
+        expect.append(sum(1 for t in range(lay.N) for u in range(lay.N) if owner[u] in kept[owner[t]]))
+    tot, per_head = attention.kept_pairs(lay, rp, ci, lay.Nb)
+    assert per_head.tolist() == expect and tot == sum(expect)
+
+
 # --------------------------------------------------------------- Hilbert order
 # The curve's defining properties, each of which a plausible slip breaks: a
 # bijection onto the cube (a lost bit), unit steps between consecutive points
@@ -374,3 +397,39 @@ def test_augmentation_ties_among_zero_masses_go_to_lower_rows():
     assert list(np.diff(ref["row_ptr"])) == [16, 16, 11] + [9] * 13
     cols = ref["col_idx"]
     assert list(cols[:16]) == list(range(16)) and list(cols[32:43]) == list(range(11))
+
+
+# ------------------------------------------------------- non-finite inputs
+def test_nonfinite_scores_keep_every_block_in_order():
+    """Reading for non-finite inputs: a NaN or infinite token makes its
+    block's pooled vector non-finite; every softmax row that then holds a
+    non-finite score is NaN, no prefix reaches p, and the row keeps all
+    blocks in block order (no augmentation candidates).  Rows untouched by
+    the token keep their normal lists."""
+    lay = BlockLayout((2, 8, 16), (1, 8, 8))             # 4 blocks of 64 tokens
+    rng = np.random.default_rng(77)
+    q = rng.normal(size=(lay.N, 16))
+    k = rng.normal(size=(lay.N, 16))
+    clean = routing.route_head(q, k, lay, 0.5, 1)
+    q_bad = q.copy()
+    q_bad[lay.members[2][5], 3] = np.nan                   # query block 2 only
+    r = routing.route_head(q_bad, k, lay, 0.5, 1)
+    assert r["base"][2] == lay.Nb and r["order"][2].tolist() == list(range(lay.Nb))
+    for i in (0, 1, 3):
+        assert r["base"][i] == clean["base"][i] and np.array_equal(r["order"][i], clean["order"][i])
+    k_bad = k.copy()
+    k_bad[lay.members[1][0], 0] = np.nan                    # key block 1: a NaN score in every row
+    r = routing.route_head(q, k_bad, lay, 0.5, 1)
+    assert np.all(r["base"] == lay.Nb)
+    assert np.array_equal(r["order"], np.tile(np.arange(lay.Nb), (lay.Nb, 1)))
+    # an infinite key coordinate makes a row's score +inf (a NaN row) or
+    # -inf (a zero mass in an otherwise finite row), by the sign of q-bar
+    k_inf = k.copy()
+    k_inf[lay.members[1][0], 0] = np.inf
+    r = routing.route_head(q, k_inf, lay, 0.5, 1)
+    qbar0 = np.array([q[m, 0].mean() for m in lay.members])
+    for i in range(lay.Nb):
+        if qbar0[i] > 0:
+            assert r["base"][i] == lay.Nb and r["order"][i].tolist() == list(range(lay.Nb))
+        else:
+            assert np.isfinite(r["P"][i]).all() and r["P"][i, 1] == 0.0
