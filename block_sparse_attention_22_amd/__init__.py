@@ -28,6 +28,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfvattn.so")
 
 FVA_OK, FVA_ERR_INVALID_ARG, FVA_ERR_UNSUPPORTED, FVA_ERR_WORKSPACE, FVA_ERR_HIP = 0, -1, -2, -3, -4
+FVA_ERR_SCRATCH = -5
+STATIC_SCRATCH_BYTES = 64 << 20     # FVA_STATIC_SCRATCH_BYTES
 FVA_BF16, FVA_F32 = 0, 1
 BUDGET_MODES = {"none": 0, "frac": 1, "match_max": 2}
 
@@ -71,7 +73,8 @@ class CtaStat(ctypes.Structure):
                 ("blocks", ctypes.c_uint32), ("t_start", ctypes.c_uint64), ("t_end", ctypes.c_uint64)]
 
 
-EXPORTS = ("fva_num_blocks", "fva_block_sizes", "fva_hilbert_order", "fva_lists_capacity", "fva_route_workspace_bytes", "fva_route",
+EXPORTS = ("fva_num_blocks", "fva_block_sizes", "fva_hilbert_order", "fva_lists_capacity", "fva_route_workspace_bytes",
+           "fva_route", "fva_route_static",
            "fva_attn_workspace_bytes", "fva_attn_stats_bytes", "fva_attn_prepare", "fva_sparse_attn",
            "fva_status_string")
 
@@ -109,6 +112,9 @@ def load_library(path: Optional[str] = None):
         lib.fva_route.argtypes = [P(Problem), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double, ctypes.c_int32,
                                   Budget, P(ListsC), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         lib.fva_route.restype = ctypes.c_int
+        lib.fva_route_static.argtypes = [P(Problem), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double,
+                                         ctypes.c_int32, Budget, P(ListsC), ctypes.c_void_p]
+        lib.fva_route_static.restype = ctypes.c_int
         lib.fva_attn_workspace_bytes.argtypes = [P(Problem), P(AttnOptions)]
         lib.fva_attn_workspace_bytes.restype = ctypes.c_size_t
         lib.fva_attn_stats_bytes.argtypes = [P(Problem), P(AttnOptions)]
@@ -286,12 +292,7 @@ def _budget(budget) -> Budget:
     return Budget(BUDGET_MODES[mode], float(frac))
 
 
-def route(q: torch.Tensor, k: torch.Tensor, p: float, kmin: int, budget=None, *, grid, tile=None,
-          order: Optional[torch.Tensor] = None,
-          want_mask: bool = False, out: Optional[BlockLists] = None) -> BlockLists:
-    """Sparse-routing front end (fva_route): per-head CSR block lists.
-
-    Runs on the current stream with that stream's routing workspace."""
+def _route_setup(q, k, grid, tile, order, want_mask, out):
     _check_device_tensor("q", q)
     _check_device_tensor("k", k)
     if q.shape != k.shape or q.dtype != k.dtype or q.stride() != k.stride():
@@ -315,6 +316,17 @@ def route(q: torch.Tensor, k: torch.Tensor, p: float, kmin: int, budget=None, *,
             head_kept=torch.empty(max(1, B * H), dtype=torch.int32, device=dev),
             mask=torch.empty(max(1, R * words), dtype=torch.int32, device=dev) if want_mask else None,
             nq=nb, nk=nb, grid=tuple(grid), tile=tuple(tile) if tile is not None else None, order=order)
+    return lib, prob, out
+
+
+def route(q: torch.Tensor, k: torch.Tensor, p: float, kmin: int, budget=None, *, grid, tile=None,
+          order: Optional[torch.Tensor] = None,
+          want_mask: bool = False, out: Optional[BlockLists] = None) -> BlockLists:
+    """Sparse-routing front end (fva_route): per-head CSR block lists.
+
+    Runs on the current stream with that stream's routing workspace."""
+    lib, prob, out = _route_setup(q, k, grid, tile, order, want_mask, out)
+    dev = q.device
     wsb = lib.fva_route_workspace_bytes(ctypes.byref(prob))
     ws = _workspace(wsb, dev, "route")
     lc = out.as_c()
@@ -322,6 +334,21 @@ def route(q: torch.Tensor, k: torch.Tensor, p: float, kmin: int, budget=None, *,
                        ctypes.byref(lc), ws.data_ptr(), ws.numel(), _stream(dev))
     if st != FVA_OK:
         raise FvaError(st, "fva_route")
+    return out
+
+
+def route_static(q: torch.Tensor, k: torch.Tensor, p: float, kmin: int, budget=None, *, grid, tile=None,
+                 order: Optional[torch.Tensor] = None, out: BlockLists) -> BlockLists:
+    """fva_route_static: ``route`` into caller-allocated ``out`` lists with the
+    library's static per-device scratch (no allocation of any kind; problems
+    whose routing workspace exceeds STATIC_SCRATCH_BYTES raise FVA_ERR_SCRATCH).
+    Calls that overlap on one device race; keep them on one stream."""
+    lib, prob, out = _route_setup(q, k, grid, tile, order, False, out)
+    lc = out.as_c()
+    st = lib.fva_route_static(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), float(p), int(kmin),
+                              _budget(budget), ctypes.byref(lc), _stream(q.device))
+    if st != FVA_OK:
+        raise FvaError(st, "fva_route_static")
     return out
 
 
@@ -474,5 +501,5 @@ def per_cu_imbalance(ctas, num_cus: int):
     return (max(busy.values()) / mean if mean > 0 else 1.0), busy
 
 
-__all__ = ["route", "sparse_attn", "BlockLists", "make_problem", "num_blocks", "block_sizes", "load_library", "FvaError",
+__all__ = ["route", "route_static", "sparse_attn", "BlockLists", "make_problem", "num_blocks", "block_sizes", "load_library", "FvaError",
            "stats_bytes", "parse_stats", "attn_prepare", "release_workspaces", "FVA_ATTN_PREPARED", "hilbert_order", "per_cu_imbalance", "lists_from_csr", "EXPORTS", "LIB_PATH"]

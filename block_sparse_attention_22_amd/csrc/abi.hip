@@ -112,6 +112,30 @@ int device_cus() {
     return g_dev_cus[dev];
 }
 
+// ------------------------------------------- static routing scratch
+// Scratch of fva_route_static: one array per device, sized for a one-GPU
+// head shard of the 720p layer (5 heads x 660 blocks need 33 MB).  The
+// array's name is a host-side stand-in; kernels get the device address that
+// hipGetSymbolAddress returns for the current device, fetched once per
+// device and kept.
+__device__ __align__(256) static char scratch[FVA_STATIC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64] = {nullptr};
+
+fva_status static_scratch(void **ptr) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return FVA_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FVA_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return FVA_OK;
+}
+
 // ------------------------------------------------------ route workspace
 struct RouteWs {
     size_t qbar, kbar, sp, order, base, add, head_base, head_kept, total;
@@ -289,9 +313,16 @@ size_t fva_route_workspace_bytes(const fva_problem *prob) {
     return route_layout(g).total;
 }
 
-fva_status fva_route(const fva_problem *prob, const void *q, const void *k, double p, int32_t kmin,
-                     fva_budget budget, const fva_lists *out, void *ws, size_t ws_bytes, void *stream) {
-    Geo g;
+}  // extern "C"
+
+namespace fva {
+namespace {
+
+// Argument checks of fva_route and fva_route_static (everything but the
+// workspace).
+fva_status route_args(const fva_problem *prob, const void *q, const void *k, double p, int32_t kmin,
+                      fva_budget budget, const fva_lists *out, Geo *gout) {
+    Geo &g = *gout;
     fva_status st = make_geo(prob, &g);
     if (st != FVA_OK) return st;
     if (!(p > 0.0 && p <= 1.0)) return FVA_ERR_INVALID_ARG;
@@ -303,11 +334,15 @@ fva_status fva_route(const fva_problem *prob, const void *q, const void *k, doub
     if (out->base_count && !aligned4(out->base_count)) return FVA_ERR_INVALID_ARG;
     if (out->head_kept && !aligned4(out->head_kept)) return FVA_ERR_INVALID_ARG;
     if (out->mask && !aligned4(out->mask)) return FVA_ERR_INVALID_ARG;
+    if (g.BH != 0 && (!aligned16(q) || !aligned16(k))) return FVA_ERR_INVALID_ARG;
+    return FVA_OK;
+}
+
+// The routing launches on a checked problem and a large enough workspace.
+fva_status route_launch(const Geo &g, const void *q, const void *k, double p, int32_t kmin, fva_budget budget,
+                        const fva_lists *out, void *ws, hipStream_t s) {
     const bool empty = (g.BH == 0);
-    if (!empty && (!aligned16(q) || !aligned16(k))) return FVA_ERR_INVALID_ARG;
     const RouteWs L = route_layout(g);
-    if (!ws || ws_bytes < L.total || ((uintptr_t)ws % kAlign)) return FVA_ERR_WORKSPACE;
-    hipStream_t s = (hipStream_t)stream;
     char *W = static_cast<char *>(ws);
     double *qbar = (double *)(W + L.qbar), *kbar = (double *)(W + L.kbar), *SP = (double *)(W + L.sp);
     int32_t *order = (int32_t *)(W + L.order), *base = (int32_t *)(W + L.base), *add = (int32_t *)(W + L.add);
@@ -323,6 +358,32 @@ fva_status fva_route(const fva_problem *prob, const void *q, const void *k, doub
     FVA_TRY_HIP(launch_csr(g, order, base, add, head_kept, out->row_ptr, out->col_idx, out->base_count, out->mask,
                            s));
     return FVA_OK;
+}
+
+}  // namespace
+}  // namespace fva
+
+extern "C" {
+
+fva_status fva_route(const fva_problem *prob, const void *q, const void *k, double p, int32_t kmin,
+                     fva_budget budget, const fva_lists *out, void *ws, size_t ws_bytes, void *stream) {
+    Geo g;
+    const fva_status st = route_args(prob, q, k, p, kmin, budget, out, &g);
+    if (st != FVA_OK) return st;
+    if (!ws || ws_bytes < route_layout(g).total || ((uintptr_t)ws % kAlign)) return FVA_ERR_WORKSPACE;
+    return route_launch(g, q, k, p, kmin, budget, out, ws, (hipStream_t)stream);
+}
+
+fva_status fva_route_static(const fva_problem *prob, const void *q, const void *k, double p, int32_t kmin,
+                            fva_budget budget, const fva_lists *out, void *stream) {
+    Geo g;
+    fva_status st = route_args(prob, q, k, p, kmin, budget, out, &g);
+    if (st != FVA_OK) return st;
+    if (route_layout(g).total > FVA_STATIC_SCRATCH_BYTES) return FVA_ERR_SCRATCH;
+    void *ws = nullptr;
+    st = static_scratch(&ws);
+    if (st != FVA_OK) return st;
+    return route_launch(g, q, k, p, kmin, budget, out, ws, (hipStream_t)stream);
 }
 
 size_t fva_attn_workspace_bytes(const fva_problem *prob, const fva_attn_options *opts) {
@@ -409,6 +470,8 @@ const char *fva_status_string(fva_status s) {
         case FVA_ERR_UNSUPPORTED: return "FVA_ERR_UNSUPPORTED: unsupported head_dim, dtype, tile volume or block count";
         case FVA_ERR_WORKSPACE: return "FVA_ERR_WORKSPACE: workspace missing, misaligned or too small";
         case FVA_ERR_HIP: return "FVA_ERR_HIP: HIP runtime error";
+        case FVA_ERR_SCRATCH:
+            return "FVA_ERR_SCRATCH: the problem needs more than FVA_STATIC_SCRATCH_BYTES of routing scratch";
     }
     return "unknown fva_status";
 }

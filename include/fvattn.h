@@ -53,7 +53,8 @@ typedef enum {
     FVA_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, bad size or parameter */
     FVA_ERR_UNSUPPORTED = -2,   /* valid but not implemented (head_dim, dtype, tile volume) */
     FVA_ERR_WORKSPACE = -3,     /* workspace smaller than the matching *_workspace_bytes */
-    FVA_ERR_HIP = -4            /* a HIP runtime call or launch failed */
+    FVA_ERR_HIP = -4,           /* a HIP runtime call or launch failed */
+    FVA_ERR_SCRATCH = -5        /* fva_route_static: the problem needs more than FVA_STATIC_SCRATCH_BYTES */
 } fva_status;
 
 typedef enum { FVA_BF16 = 0, FVA_F32 = 1 } fva_dtype;
@@ -218,6 +219,23 @@ size_t fva_route_workspace_bytes(const fva_problem *prob);
  */
 fva_status fva_route(const fva_problem *prob, const void *q, const void *k, double p, int32_t kmin,
                      fva_budget budget, const fva_lists *out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * fva_route without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, results and checks as fva_route;
+ * the scratch is instead a static device array of FVA_STATIC_SCRATCH_BYTES
+ * that the library holds on every device it runs on until the process ends
+ * (a one-GPU head shard of the 720p layer, 5 heads x 660 blocks, needs
+ * 33 MB).  Problems with fva_route_workspace_bytes(prob) above that size
+ * return FVA_ERR_SCRATCH before anything is launched.  Nothing is allocated:
+ * no hipMalloc, hipFree or allocating library call.  All calls on one device
+ * share its array (every buffer in it is fully rewritten by each call), so
+ * calls that overlap on one device race: order them, e.g. on one stream.
+ */
+#define FVA_STATIC_SCRATCH_BYTES (64u << 20)
+fva_status fva_route_static(const fva_problem *prob, const void *q, const void *k, double p, int32_t kmin,
+                            fva_budget budget, const fva_lists *out, void *stream);
 
 /* Workspace bytes fva_sparse_attn needs for these options (NULL = defaults).
  * With num_ctas == 0 this queries the current device (0 if that fails). */

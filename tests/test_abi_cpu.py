@@ -287,3 +287,19 @@ def test_token_order_problems(lib):
     assert fva.num_blocks((21, 45, 80), None, ordered=True) == 591
     sz = fva.block_sizes((21, 45, 80), None, ordered=True)
     assert len(sz) == 591 and sz.sum() == 75600 and sz[-1] == 80
+
+
+def test_route_static_rejects_oversized_problems_before_launching(lib):
+    """fva_route_static checks the problem against its static scratch on the
+    host: the 40-head 720p layer needs 264 MB of routing scratch, more than
+    FVA_STATIC_SCRATCH_BYTES, and is refused before any device call."""
+    p = prob()
+    assert lib.fva_route_workspace_bytes(ctypes.byref(p)) > fva.STATIC_SCRATCH_BYTES
+    fake = 1 << 20                                   # aligned, never dereferenced
+    lists = ListsC(fake, fake, None, None, None)
+    st = lib.fva_route_static(ctypes.byref(p), fake, fake, 0.9, 8, Budget(1, 0.1), ctypes.byref(lists), None)
+    assert st == fva.FVA_ERR_SCRATCH
+    assert b"FVA_ERR_SCRATCH" in lib.fva_status_string(st)
+    five = prob(heads=5, stride_b=5 * 75600 * 128)    # one GPU's 5-head shard fits
+    assert lib.fva_route_workspace_bytes(ctypes.byref(five)) <= fva.STATIC_SCRATCH_BYTES
+
