@@ -303,3 +303,27 @@ def test_route_static_rejects_oversized_problems_before_launching(lib):
     five = prob(heads=5, stride_b=5 * 75600 * 128)    # one GPU's 5-head shard fits
     assert lib.fva_route_workspace_bytes(ctypes.byref(five)) <= fva.STATIC_SCRATCH_BYTES
 
+
+
+def test_per_cu_imbalance_of_synthetic_records():
+    """The host reduction of the per-workgroup records: busy time summed per
+    compute unit (HW_ID CU/SH/SE fields and XCC_ID), then max over mean over
+    all compute units.  Equal loads give exactly 1; one CU with twice the
+    work of the others gives 2 / (1 + 1/n); a CU that ran nothing counts as
+    idle in the mean."""
+    from block_sparse_attention_22_amd import CtaStat, per_cu_imbalance
+
+    def rec(xcc, cu, t0, t1):
+        return CtaStat(hw_id=(cu << 8) | 0x5, xcc_id=xcc, items=1, blocks=1, t_start=t0, t_end=t1)
+
+    n = 16
+    eq = [rec(x, c, 100, 200) for x in range(4) for c in range(4)] + \
+         [rec(x, c, 300, 400) for x in range(4) for c in range(4)]          # two workgroups per CU
+    imb, busy = per_cu_imbalance(eq, n)
+    assert imb == 1.0 and len(busy) == n and all(b == 200 for b in busy.values())
+    skew = [rec(x, c, 0, 200 if (x, c) == (0, 0) else 100) for x in range(4) for c in range(4)]
+    imb, _ = per_cu_imbalance(skew, n)
+    assert abs(imb - 200 / ((200 + 15 * 100) / n)) < 1e-12
+    half = [rec(0, c, 0, 100) for c in range(8)]                              # 8 of 16 CUs busy
+    imb, _ = per_cu_imbalance(half, n)
+    assert imb == 2.0

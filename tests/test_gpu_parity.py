@@ -5,6 +5,11 @@ times (default balancer options).  Block lists are compared in full; outputs
 on every row for the small workloads and on a seeded sample of query blocks
 per head for the 75,600- and 171,360-token layers.
 """
+import json
+import os
+import subprocess
+import sys
+
 import numpy as np
 import pytest
 import torch
@@ -57,14 +62,185 @@ def test_workload_parity(dev, cid):
 
     print(f"[parity] config {cid}: attention on GPU", flush=True)
     o = fva.sparse_attn(qd, kd, vd, lists)
-    o2 = fva.sparse_attn(qd, kd, vd, lists)
+    st = torch.zeros(fva.stats_bytes(qd, w.grid, w.tile), dtype=torch.uint8, device=dev)
+    o2 = fva.sparse_attn(qd, kd, vd, lists, stats=st)
     torch.cuda.synchronize()
     assert torch.equal(o, o2), "attention is not deterministic"
+    # the library's count of kept valid token pairs (the flop count) against the oracle's
+    info, _ = fva.parse_stats(st)
+    pairs, _ = attention.kept_pairs(lay, g["row_ptr"], g["col_idx"], lay.Nb)
+    print(f"[parity] config {cid}: kept pairs {info.kept_pairs} (oracle {pairs})", flush=True)
+    assert info.kept_pairs == pairs
     rows = _rows_sample(w, lay.Nb, SAMPLE[cid])
     prec = "fp64" if cid <= 2 else "fp32"
     err = attention_error(o, qn, kn, vn, lay, g["row_ptr"], g["col_idx"], rows=rows, precision=prec)
     print(f"[parity] config {cid}: max|o - oracle| = {err:.3e} (tol {TOL[w.dtype]})", flush=True)
     assert err <= TOL[w.dtype]
+
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _oracle_errors(tmp_path, cid, lay, q, k, v, o, g, rows, hilbert=False):
+    """|o - oracle| of every query block in ``rows`` [(b*H + h, i), ...],
+    computed by tests/oracle_pool.py in a child process (a pool of CPU
+    workers); returns (errors in the order of rows, worker count)."""
+    stem = str(tmp_path / f"c{cid}")
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        np.save(f"{stem}_{n}.npy", t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16
+                else t.numpy())
+    H = q.shape[1]
+    parts = []
+    for bh, i in rows:
+        b, h = divmod(bh, H)
+        parts.append(torch.as_tensor(lay.members[i], device=o.device) + (b * H + h) * lay.N)
+    flat = o.reshape(-1, o.shape[-1])
+    out = flat.index_select(0, torch.cat(parts)).float().cpu().numpy()
+    np.savez(f"{stem}.npz", cid=cid, hilbert=int(hilbert), row_ptr=g["row_ptr"], col_idx=g["col_idx"],
+             rows=np.asarray(rows, dtype=np.int64), out=out)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "tests", "oracle_pool.py"), f"{stem}.npz"],
+                       capture_output=True, text=True, timeout=1500)
+    assert r.returncode == 0, r.stderr[-3000:]
+    res = json.loads(r.stdout.strip().splitlines()[-1])
+    return np.asarray(res["err"]), res["processes"]
+
+
+def test_shard_outputs_on_every_row(dev, tmp_path):
+    """The 720p 5-head shard (every head dense after the match-max budget):
+    every output of all 3,300 query blocks against the oracle, on the GPU's
+    own lists, in the launch configuration the bench times."""
+    w = WORKLOADS[4]
+    q, k, v, _ = make_inputs(w)
+    lay = BlockLayout(w.grid, w.tile)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    lists = fva.route(qd, kd, w.p, w.kmin, w.budget, grid=w.grid, tile=w.tile)
+    o = fva.sparse_attn(qd, kd, vd, lists)
+    torch.cuda.synchronize()
+    g = gpu_lists_to_host(lists)
+    rows = [(bh, i) for bh in range(w.B * w.H) for i in range(lay.Nb)]
+    err, nproc = _oracle_errors(tmp_path, 4, lay, q, k, v, o, g, rows)
+    per_head = err.reshape(w.B * w.H, lay.Nb).max(axis=1)
+    print(f"\n[shard] {len(rows)} query blocks on {nproc} processes: max|o - oracle| per head "
+          f"{[f'{x:.2e}' for x in per_head]}", flush=True)
+    assert err.max() <= TOL["bf16"]
+
+
+def _pair_leads(sizes):
+    """First blocks of the greedy pairs of neighbouring <= 64-token blocks."""
+    small = np.asarray(sizes) <= 64
+    lead, i = [], 0
+    while i < len(small) - 1:
+        if small[i] and small[i + 1]:
+            lead.append(i)
+            i += 2
+        else:
+            i += 1
+    return lead
+
+
+def test_720p_outputs_on_every_special_row(dev, tmp_path):
+    """The 720p layer where the kernel takes its special paths: every row the
+    plan splits into chunks, one paired item per head (both rows), every edge
+    class of query block (40, 64, 80 and 128 tokens; two rows of each per
+    head), plus the seeded sample of 16 rows per head; worst error per class."""
+    w = WORKLOADS[3]
+    q, k, v, _ = make_inputs(w)
+    lay = BlockLayout(w.grid, w.tile)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    lists = fva.route(qd, kd, w.p, w.kmin, w.budget, grid=w.grid, tile=w.tile)
+    st = torch.zeros(fva.stats_bytes(qd, w.grid, w.tile), dtype=torch.uint8, device=dev)
+    o = fva.sparse_attn(qd, kd, vd, lists, stats=st)
+    torch.cuda.synchronize()
+    info, _ = fva.parse_stats(st)
+    g = gpu_lists_to_host(lists)
+    rp, ci, nb, H = g["row_ptr"], g["col_idx"], lay.Nb, w.B * w.H
+    C = info.chunk_blocks
+    counts = np.diff(rp).reshape(H, nb)
+    leads = _pair_leads(lay.sizes)
+    rng = np.random.default_rng((260716190, 3, 7))
+    cls = {}
+    for bh in range(H):
+        paired = set()
+        for i in leads:
+            r = bh * nb + i
+            if len(np.union1d(ci[rp[r]:rp[r + 1]], ci[rp[r + 1]:rp[r + 2]])) <= C:
+                paired |= {i, i + 1}
+        for i in range(nb):
+            if counts[bh, i] > C and i not in paired:
+                cls.setdefault((bh, i), "split")
+        if paired:
+            i0 = min(paired)
+            cls.setdefault((bh, i0), "paired")
+            cls.setdefault((bh, i0 + 1), "paired")
+        for size in (40, 64, 80, 128):
+            cand = np.nonzero(lay.sizes == size)[0]
+            for i in rng.choice(cand, min(2, len(cand)), replace=False):
+                cls.setdefault((bh, int(i)), f"edge{size}")
+    for bh, sel in _rows_sample(w, nb, SAMPLE[3]).items():
+        for i in sel:
+            cls.setdefault((bh, int(i)), "sample")
+    n_split = sum(1 for c in cls.values() if c == "split")
+    assert n_split == info.n_split_rows, (n_split, info.n_split_rows)
+    rows = sorted(cls)
+    err, nproc = _oracle_errors(tmp_path, 3, lay, q, k, v, o, g, rows)
+    worst = {}
+    for rc, e in zip(rows, err):
+        worst[cls[rc]] = max(worst.get(cls[rc], 0.0), float(e))
+    counts_by = {c: sum(1 for x in cls.values() if x == c) for c in worst}
+    print(f"\n[720p special rows] {len(rows)} query blocks on {nproc} processes; worst |o - oracle| by class: "
+          + ", ".join(f"{c} ({counts_by[c]} rows) {worst[c]:.2e}" for c in sorted(worst)), flush=True)
+    assert set(worst) >= {"split", "paired", "edge40", "edge64", "edge80", "edge128"}
+    assert max(worst.values()) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("grid,tile,H", [((5, 20, 20), (2, 8, 8), 3), ((8, 128, 128), (1, 8, 8), 1)],
+                         ids=["27_blocks", "2048_blocks"])
+def test_route_mask_matches_the_lists(dev, grid, tile, H):
+    """The materialised mask (want_mask): bit j of row r is set exactly when
+    block j is in the row's CSR list, and no bit at or past Nk is set; on a
+    ragged grid (one partial word) and at 2,048 blocks (64 words)."""
+    q, k, _ = _small_case(grid, tile, H, 128, "bf16", 160, scale=2.0)
+    lay = BlockLayout(grid, tile)
+    lists = fva.route(q.to(dev), k.to(dev), 0.8, 2, ("frac", 0.1), grid=grid, tile=tile, want_mask=True)
+    g = gpu_lists_to_host(lists)
+    nb = lay.Nb
+    words = (nb + 31) // 32
+    R = H * nb
+    mask = lists.mask[: R * words].cpu().numpy().view(np.uint32).reshape(R, words)
+    bits = np.unpackbits(mask.view(np.uint8).reshape(R, words, 4)[..., ::-1], axis=-1)[..., ::-1]
+    bits = bits.reshape(R, words * 32)             # bits[r, j] = bit j of row r
+    for r in range(R):
+        expect = np.zeros(words * 32, dtype=np.uint8)
+        expect[g["col_idx"][g["row_ptr"][r]:g["row_ptr"][r + 1]]] = 1
+        assert np.array_equal(bits[r], expect), r
+    assert not bits[:, nb:].any()
+
+
+def test_equal_load_plan_balances_exactly(dev):
+    """A synthetic equal-load plan: 64 heads of 256 full blocks, every row
+    keeping the same 4 blocks, rows never split, so that each workgroup gets
+    32 equal items from the queues.  The plan's own prediction is exactly 1
+    and the measured per-CU imbalance stays within the 1.10 bound (a
+    workgroup that starts late leaves at most an item or so to the others)."""
+    grid, tile, H = (8, 64, 64), (2, 8, 8), 64             # 4 x 8 x 8 = 256 blocks of 128 tokens
+    q, k, v = (t.to(dev) for t in _small_case(grid, tile, H, 128, "bf16", 170))
+    nb = 256
+    st = torch.zeros(fva.stats_bytes(q, grid, tile, chunk_blocks=-1), dtype=torch.uint8, device=dev)
+    R = H * nb
+    rp = np.arange(R + 1, dtype=np.int64) * 4
+    ci = np.concatenate([np.arange(4) * 64 + (r % 64) for r in range(R)])
+    lists = fva.lists_from_csr(rp, ci, nq=nb, grid=grid, tile=tile, device=dev)
+    fva.sparse_attn(q, k, v, lists, chunk_blocks=-1, row_pairs=False)     # warm-up
+    fva.sparse_attn(q, k, v, lists, chunk_blocks=-1, row_pairs=False, stats=st)
+    torch.cuda.synchronize()
+    info, ctas = fva.parse_stats(st)
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    assert R % info.num_ctas == 0 and info.n_items == R
+    imb, busy = fva.per_cu_imbalance(ctas, ncu)
+    print(f"\n[equal load] {R} items on {info.num_ctas} workgroups: predicted {info.predicted_imbalance:.4f}, "
+          f"measured per-CU {imb:.4f}", flush=True)
+    assert info.predicted_imbalance == 1.0
+    assert imb <= 1.10
 
 
 def _small_case(grid, tile, H, d, dtype, seed, scale=1.0, B=1):
@@ -566,7 +742,7 @@ def test_two_streams_with_different_problems(dev):
         assert torch.equal(oa, ref_a) and torch.equal(ob, ref_b), rep
 
 
-@pytest.mark.parametrize("cid", [1, 2, 4])
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
 def test_hilbert_block_parity(dev, cid):
     """Hilbert-curve blocks (128-token runs of the curve order from the
     library's host helper) against the oracle's own Hilbert layout: lists by
@@ -590,6 +766,8 @@ def test_hilbert_block_parity(dev, cid):
     assert_exact(rep)
     o = fva.sparse_attn(qd, kd, vd, lists)
     torch.cuda.synchronize()
+    print(f"[parity] config {cid} hilbert: density {np.diff(g['row_ptr']).sum() / (w.B * w.H * lay.Nb ** 2):.4f} "
+          f"(tiles: see the workload test)", flush=True)
     rows = _rows_sample(w, lay.Nb, SAMPLE[cid])
     prec = "fp64" if cid <= 2 else "fp32"
     err = attention_error(o, qn, kn, vn, lay, g["row_ptr"], g["col_idx"], rows=rows, precision=prec)
