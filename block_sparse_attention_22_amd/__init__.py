@@ -76,7 +76,7 @@ class CtaStat(ctypes.Structure):
 EXPORTS = ("fva_num_blocks", "fva_block_sizes", "fva_hilbert_order", "fva_lists_capacity", "fva_route_workspace_bytes",
            "fva_route", "fva_route_static",
            "fva_attn_workspace_bytes", "fva_attn_stats_bytes", "fva_attn_prepare", "fva_sparse_attn",
-           "fva_status_string")
+           "fva_layer_workspace_bytes", "fva_layer", "fva_status_string")
 
 _lib = None
 _lib_lock = threading.Lock()
@@ -126,6 +126,12 @@ def load_library(path: Optional[str] = None):
         lib.fva_attn_prepare.argtypes = [P(Problem), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_size_t, P(AttnOptions), ctypes.c_void_p]
         lib.fva_attn_prepare.restype = ctypes.c_int
+        lib.fva_layer_workspace_bytes.argtypes = [P(Problem), P(AttnOptions)]
+        lib.fva_layer_workspace_bytes.restype = ctypes.c_size_t
+        lib.fva_layer.argtypes = [P(Problem), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double,
+                                  ctypes.c_int32, P(Budget), P(ListsC), ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_size_t, ctypes.c_void_p, P(AttnOptions), ctypes.c_void_p]
+        lib.fva_layer.restype = ctypes.c_int
         lib.fva_status_string.argtypes = [ctypes.c_int]
         lib.fva_status_string.restype = ctypes.c_char_p
         if path is None:
@@ -458,6 +464,41 @@ def sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lists: BlockL
     return out
 
 
+def layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, p: float, kmin: int, budget=None, *, grid, tile=None,
+          order: Optional[torch.Tensor] = None, lists: Optional[BlockLists] = None,
+          out: Optional[torch.Tensor] = None, stats: Optional[torch.Tensor] = None, chunk_blocks: int = 0,
+          num_ctas: int = 0, kernel_events=None, row_pairs: bool = True):
+    """route then sparse_attn in one call (fva_layer), sharing one read of q, k
+    and v for bf16, head_dim 128; returns (lists, out), bit for bit those of
+    the two calls.  Runs on the current stream with that stream's layer
+    workspace."""
+    _check_qkv(q, k, v)
+    lib, prob, lists = _route_setup(q, k, grid, tile, order, False, lists)
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    if out.stride() != q.stride() or out.dtype != q.dtype:
+        raise ValueError("out must match q's strides and dtype")
+    opts = attn_options(chunk_blocks, num_ctas, kernel_events, False, row_pairs)
+    wsb = lib.fva_layer_workspace_bytes(ctypes.byref(prob), ctypes.byref(opts))
+    if wsb == 0:
+        raise FvaError(FVA_ERR_INVALID_ARG, "fva_layer_workspace_bytes")
+    ws = _workspace(wsb, q.device, "layer")
+    sp = None
+    if stats is not None:
+        need = lib.fva_attn_stats_bytes(ctypes.byref(prob), ctypes.byref(opts))
+        if stats.numel() * stats.element_size() < need:
+            raise ValueError(f"stats buffer needs {need} bytes")
+        sp = stats.data_ptr()
+    lc = lists.as_c()
+    bud = _budget(budget)
+    st = lib.fva_layer(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), float(p), int(kmin),
+                       ctypes.byref(bud), ctypes.byref(lc), out.data_ptr(), ws.data_ptr(), ws.numel(), sp,
+                       ctypes.byref(opts), _stream(q.device))
+    if st != FVA_OK:
+        raise FvaError(st, "fva_layer")
+    return lists, out
+
+
 def lists_from_csr(row_ptr, col_idx, *, nq, grid, tile=None, device, order=None) -> BlockLists:
     """Wrap host CSR arrays (e.g. lists made elsewhere) as device BlockLists."""
     rp = torch.as_tensor(row_ptr, dtype=torch.int32).to(device)
@@ -501,5 +542,5 @@ def per_cu_imbalance(ctas, num_cus: int):
     return (max(busy.values()) / mean if mean > 0 else 1.0), busy
 
 
-__all__ = ["route", "route_static", "sparse_attn", "BlockLists", "make_problem", "num_blocks", "block_sizes", "load_library", "FvaError",
+__all__ = ["route", "route_static", "sparse_attn", "layer", "BlockLists", "make_problem", "num_blocks", "block_sizes", "load_library", "FvaError",
            "stats_bytes", "parse_stats", "attn_prepare", "release_workspaces", "FVA_ATTN_PREPARED", "hilbert_order", "per_cu_imbalance", "lists_from_csr", "EXPORTS", "LIB_PATH"]

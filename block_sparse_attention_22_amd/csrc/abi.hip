@@ -340,7 +340,7 @@ fva_status route_args(const fva_problem *prob, const void *q, const void *k, dou
 
 // The routing launches on a checked problem and a large enough workspace.
 fva_status route_launch(const Geo &g, const void *q, const void *k, double p, int32_t kmin, fva_budget budget,
-                        const fva_lists *out, void *ws, hipStream_t s) {
+                        const fva_lists *out, void *ws, hipStream_t s, bool pooled = false) {
     const bool empty = (g.BH == 0);
     const RouteWs L = route_layout(g);
     char *W = static_cast<char *>(ws);
@@ -349,8 +349,10 @@ fva_status route_launch(const Geo &g, const void *q, const void *k, double p, in
     int32_t *head_base = (int32_t *)(W + L.head_base);
     int32_t *head_kept = out->head_kept ? out->head_kept : (int32_t *)(W + L.head_kept);
     if (!empty) {
-        FVA_TRY_HIP(launch_pool(g, q, qbar, s));
-        FVA_TRY_HIP(launch_pool(g, k, kbar, s));
+        if (!pooled) {
+            FVA_TRY_HIP(launch_pool(g, q, qbar, s));
+            FVA_TRY_HIP(launch_pool(g, k, kbar, s));
+        }
         FVA_TRY_HIP(launch_scores(g, qbar, kbar, SP, s));
         FVA_TRY_HIP(launch_row_select(g, SP, order, base, p, kmin, s));
         FVA_TRY_HIP(launch_augment(g, SP, base, add, head_base, head_kept, budget.mode, budget.frac, s));
@@ -402,22 +404,18 @@ size_t fva_attn_stats_bytes(const fva_problem *prob, const fva_attn_options *opt
     return sizeof(fva_plan_info) + (size_t)sz.num_ctas * sizeof(fva_cta_stat);
 }
 
-fva_status fva_sparse_attn(const fva_problem *prob, const void *q, const void *k, const void *v,
-                           const fva_lists *lists, void *o, void *ws, size_t ws_bytes, void *stats,
-                           const fva_attn_options *opts, void *stream) {
-    Geo g;
-    fva_status st = make_geo(prob, &g);
-    if (st != FVA_OK) return st;
-    if (!lists || !aligned4(lists->row_ptr) || !aligned4(lists->col_idx)) return FVA_ERR_INVALID_ARG;
-    AttnPlanSizes sz;
-    st = attn_sizes(g, opts, &sz);
-    if (st != FVA_OK) return st;
-    if (g.BH == 0) return FVA_OK;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FVA_ERR_INVALID_ARG;
-    if (stats && ((uintptr_t)stats & 7u)) return FVA_ERR_INVALID_ARG;
+}  // extern "C"
+
+namespace fva {
+namespace {
+
+// The attention launches on a checked problem and a large enough workspace
+// (everything of fva_sparse_attn after its checks); prepared: the K/V copies
+// are already in the workspace.
+fva_status attn_launch(const Geo &g, const AttnPlanSizes &sz, const void *q, const void *k, const void *v,
+                       const fva_lists *lists, void *o, void *ws, void *stats, const fva_attn_options *opts,
+                       bool prepared, hipStream_t s) {
     const AttnWs L = attn_layout(g, sz);
-    if (!ws || ws_bytes < L.total || ((uintptr_t)ws % kAlign)) return FVA_ERR_WORKSPACE;
-    hipStream_t s = (hipStream_t)stream;
     char *W = static_cast<char *>(ws);
     int32_t *tok = (int32_t *)(W + L.tok), *bsize = (int32_t *)(W + L.bsize);
     PlanHeader *hdr = (PlanHeader *)(W + L.hdr);
@@ -425,8 +423,7 @@ fva_status fva_sparse_attn(const fva_problem *prob, const void *q, const void *k
     SplitRow *splits = (SplitRow *)(W + L.splits);
     float *part_o = (float *)(W + L.part_o), *part_ml = (float *)(W + L.part_ml);
     const int chunk = opts ? opts->chunk_blocks : 0;
-    if (!(opts && (opts->flags & FVA_ATTN_PREPARED)))
-        FVA_TRY_HIP(launch_pack_kv(g, k, v, (uint16_t *)(W + L.kp), (uint16_t *)(W + L.vt), s));
+    if (!prepared) FVA_TRY_HIP(launch_pack_kv(g, k, v, (uint16_t *)(W + L.kp), (uint16_t *)(W + L.vt), s));
     // Pairs of small query blocks, unless fixed chunks or the flag say otherwise.
     const bool pair_rows = sz.max_pairs > 0 && chunk <= 0 && !(opts && (opts->flags & FVA_ATTN_NO_ROW_PAIRS));
     const RowPairs rp{pair_rows ? sz.max_pairs : 0, (int32_t *)(W + L.role), (int32_t *)(W + L.first),
@@ -444,6 +441,94 @@ fva_status fva_sparse_attn(const fva_problem *prob, const void *q, const void *k
                                  ev0, ev1, s));
     FVA_TRY_HIP(launch_combine(g, o, tok, bsize, hdr, splits, part_o, part_ml, sz.cap_splits, s));
     return FVA_OK;
+}
+
+// Argument checks of fva_sparse_attn and fva_layer on the attention side
+// (everything but the workspace).
+fva_status attn_args(const Geo &g, const void *q, const void *k, const void *v, const fva_lists *lists, void *o,
+                     void *stats) {
+    if (!lists || !aligned4(lists->row_ptr) || !aligned4(lists->col_idx)) return FVA_ERR_INVALID_ARG;
+    if (g.BH == 0) return FVA_OK;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FVA_ERR_INVALID_ARG;
+    if (stats && ((uintptr_t)stats & 7u)) return FVA_ERR_INVALID_ARG;
+    return FVA_OK;
+}
+
+// fva_layer's workspace: the routing workspace, then the attention's.
+struct LayerWs {
+    size_t route, attn, total;
+};
+
+LayerWs layer_layout(const Geo &g, const AttnPlanSizes &sz) {
+    LayerWs w;
+    w.route = 0;
+    w.attn = align_up(route_layout(g).total);
+    w.total = w.attn + attn_layout(g, sz).total;
+    return w;
+}
+
+}  // namespace
+}  // namespace fva
+
+extern "C" {
+
+fva_status fva_sparse_attn(const fva_problem *prob, const void *q, const void *k, const void *v,
+                           const fva_lists *lists, void *o, void *ws, size_t ws_bytes, void *stats,
+                           const fva_attn_options *opts, void *stream) {
+    Geo g;
+    fva_status st = make_geo(prob, &g);
+    if (st != FVA_OK) return st;
+    AttnPlanSizes sz;
+    st = attn_sizes(g, opts, &sz);
+    if (st != FVA_OK) return st;
+    st = attn_args(g, q, k, v, lists, o, stats);
+    if (st != FVA_OK || g.BH == 0) return st;
+    if (!ws || ws_bytes < attn_layout(g, sz).total || ((uintptr_t)ws % kAlign)) return FVA_ERR_WORKSPACE;
+    return attn_launch(g, sz, q, k, v, lists, o, ws, stats, opts, opts && (opts->flags & FVA_ATTN_PREPARED),
+                       (hipStream_t)stream);
+}
+
+size_t fva_layer_workspace_bytes(const fva_problem *prob, const fva_attn_options *opts) {
+    Geo g;
+    if (make_geo(prob, &g) != FVA_OK) return 0;
+    AttnPlanSizes sz;
+    if (attn_sizes(g, opts, &sz) != FVA_OK) return 0;
+    return layer_layout(g, sz).total;
+}
+
+fva_status fva_layer(const fva_problem *prob, const void *q, const void *k, const void *v, double p, int32_t kmin,
+                     const fva_budget *budget_ptr, const fva_lists *lists, void *o, void *ws, size_t ws_bytes,
+                     void *stats, const fva_attn_options *opts, void *stream) {
+    if (!budget_ptr) return FVA_ERR_INVALID_ARG;
+    const fva_budget budget = *budget_ptr;
+    Geo g;
+    fva_status st = route_args(prob, q, k, p, kmin, budget, lists, &g);
+    if (st != FVA_OK) return st;
+    AttnPlanSizes sz;
+    st = attn_sizes(g, opts, &sz);
+    if (st != FVA_OK) return st;
+    if (opts && (opts->flags & FVA_ATTN_PREPARED)) return FVA_ERR_INVALID_ARG;
+    st = attn_args(g, q, k, v, lists, o, stats);
+    if (st != FVA_OK) return st;
+    const LayerWs L = layer_layout(g, sz);
+    if (!ws || ws_bytes < L.total || ((uintptr_t)ws % kAlign)) return FVA_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    char *W = static_cast<char *>(ws);
+    void *rws = W + L.route, *aws = W + L.attn;
+    // bf16, d = 128: one prologue reads Q, K and V once for the routing's
+    // pooled means and the attention's K/V copies; otherwise the two calls'
+    // own steps, back to back.
+    const bool fused = uses_packed_kv(g) && g.BH > 0;
+    if (fused) {
+        const RouteWs R = route_layout(g);
+        const AttnWs A = attn_layout(g, sz);
+        char *RW = static_cast<char *>(rws), *AW = static_cast<char *>(aws);
+        FVA_TRY_HIP(launch_prologue(g, q, k, v, (double *)(RW + R.qbar), (double *)(RW + R.kbar),
+                                    (uint16_t *)(AW + A.kp), (uint16_t *)(AW + A.vt), s));
+    }
+    st = route_launch(g, q, k, p, kmin, budget, lists, rws, s, fused);
+    if (st != FVA_OK || g.BH == 0) return st;
+    return attn_launch(g, sz, q, k, v, lists, o, aws, stats, opts, fused, s);
 }
 
 fva_status fva_attn_prepare(const fva_problem *prob, const void *k, const void *v, void *ws, size_t ws_bytes,

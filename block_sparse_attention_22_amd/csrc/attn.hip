@@ -13,13 +13,14 @@
 //                         than a chunk size are split so that no item
 //                         dominates a compute unit's share; a pair whose union
 //                         fits the chunk size is one item
-//   pack_kv_kernel        block-major K and V^T copies (bf16, d = 128)
+//   pack_kv_kernel        block-major K and group-major V^T copies (bf16, d = 128)
 //   attn_bf16_d128_kernel bf16, d = 128: two persistent workgroups per CU
 //                         pull items from per-XCD queues (runs of 8 items
 //                         dealt round robin to the 8 XCDs); per item (one
 //                         query block, or a pair on waves 0-1 and 2-3) an
-//                         online-softmax flash loop over the kept key blocks,
-//                         64 keys per step, K/V^T streamed by LDS-DMA, bf16
+//                         online-softmax flash loop over the valid keys of
+//                         the kept blocks, 64 keys per step (a step may span
+//                         blocks), K/V^T streamed by LDS-DMA, bf16
 //                         MFMA (v_mfma_f32_32x32x16_bf16) for Q K^T and P V
 //   attn_bf16_kernel      the same for d = 64 (K/V staged through registers)
 //   attn_f32_kernel       the same contract in float32 arithmetic
@@ -420,23 +421,22 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
 // Head dimension 128, bf16: the production kernel.
 //
 // Two workgroups per CU (two waves per SIMD), so one wave's softmax overlaps
-// the other wave's matrix work.  Keys are consumed in 64-key half blocks held
-// in a two-stage LDS ring (2 x (16 KB K + 16 KB V^T) per workgroup), filled by
-// LDS-DMA buffer loads issued one half block ahead from the block-major K and
-// V^T copies that pack_kv_kernel writes (every DMA address is a per-lane
+// the other wave's matrix work.  Keys are consumed in 64-key chunks held in a
+// two-stage LDS ring (2 x (16 KB K + 16 KB V^T) per workgroup), filled by
+// LDS-DMA buffer loads issued one chunk ahead from the block-major K and
+// group-major V^T copies that pack_kv_kernel writes (every DMA address is a per-lane
 // constant plus a wave-uniform block offset, with no per-lane index loads).
 // Work items come from per-XCD queues (next_item_xcd).  The softmax offset
-// of a row (log2 units) is lazy: a half block's probabilities are first
+// of a row (log2 units) is lazy: a chunk's probabilities are first
 // formed against the current offset, and only when one of them could exceed
 // 2^16 (a lane's sum of them does; always true on an item's first half,
 // where the offset is -inf) is the offset raised to the exact running max,
-// the accumulator rescaled and the half recomputed.  The row max is thus
-// computed on a few halves per row instead of on every half, and no
+// the accumulator rescaled and the chunk recomputed.  The row max is thus
+// computed on a few chunks per row instead of on every chunk, and no
 // probability exceeds 2^16.  Any offset is exact, since numerator and
 // denominator use the same one; the denominator sums the bf16-rounded
 // probabilities that P V uses, so that the two see identical weights.
-constexpr int kHalf = 64;                        // keys per half block
-constexpr int kHalfBytes = kHalf * 128 * 2;      // 16 KB: K or V^T of one half block
+constexpr int kChunk = 64;                       // keys per step
 constexpr float kLazyBound = 65536.0f;           // largest probability the fast path admits
 
 // Lane l and lane l ^ 32 (the two halves of one query's keys) combined by a
@@ -444,7 +444,7 @@ constexpr float kLazyBound = 65536.0f;           // largest probability the fast
 __device__ __forceinline__ float max_halves(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
 __device__ __forceinline__ float sum_halves(float x) { return x + __shfl_xor(x, 32, 64); }
 
-// Probabilities of one wave's 64-key half block against the offset m:
+// Probabilities of one wave's 64-key chunk against the offset m:
 // p = exp2(s * c - m), rounded to bf16 into the B operands of P V; returns
 // this lane's sum of the ROUNDED values (v_dot2 with a pair of ones, two
 // partial sums).
@@ -470,41 +470,44 @@ __device__ __forceinline__ float half_probs(const f32x16 *sacc, float c, float m
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
-// K half block: [64 slots][128] bf16, 16-byte chunk c of row s at c ^ f(s).
+// K stage: [64 keys][128] bf16, 16-byte chunk c of row s at c ^ f(s).
 __device__ __forceinline__ int kpos128(int slot, int c) { return c ^ ((slot ^ (slot >> 3)) & 15); }
-// V^T half block: [128 dd][64 slots] bf16, 8-slot group g of row dd at g ^ ((dd >> 1) & 7).
-__device__ __forceinline__ int vpos128(int dd, int g) { return g ^ ((dd >> 1) & 7); }
 
-// LDS-DMA of one half block of packed block j: 4 + 4 wave instructions of
-// 1 KB (piece i < 4: K rows, else V^T rows); each lane fetches the 16-byte
-// chunk that the swizzle places at its LDS position.
-// Per-lane byte offsets of this wave's DMA pieces within one half block of a
-// packed block (K rows: piece i < 4; V^T rows: piece i >= 4); the block and
-// half add a wave-uniform offset.
+// V stage: [8 key groups][128 dd][8 keys] bf16 (V^T per group of 8 keys, the
+// layout of the packed copy), so that an 8-key group is 2 KB contiguous in
+// both places.
+
+// A chunk is 64 consecutive keys of the item's stream: the valid keys of its
+// kept blocks in list order, each block rounded up to whole 8-key groups
+// (the keys of the round-up are masked).  Wave w fetches groups 2w and 2w + 1
+// of a chunk: K rows 16w .. 16w + 15 (four 1 KB pieces of 4 rows) and the V
+// groups (four 1 KB pieces of 64 dd rows).  A group never spans two blocks,
+// so every piece is one contiguous run of one block's packed copy: a per-lane
+// constant offset plus a wave-uniform base.
 struct DmaLane {
-    int off[8];
+    int k[4];     // K piece p: source row 4 (p & 1) + lane / 16 of the group, chunk swizzled for LDS row 16w + 4p + lane / 16
+    int v;        // V pieces: 16 bytes per lane (64 dd rows of 8 keys)
 };
 
 __device__ __forceinline__ DmaLane dma_lane(int w, int lane) {
     DmaLane d;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int seg = 4 * w + i;
-        const int slot = 4 * seg + (lane >> 4);
-        const int ck = (lane & 15) ^ ((slot ^ (slot >> 3)) & 15);
-        d.off[i] = slot * 256 + ck * 16;
-        const int dd = 8 * seg + (lane >> 3);
-        const int gv = (lane & 7) ^ ((dd >> 1) & 7);
-        d.off[4 + i] = dd * 256 + 8 * gv * 2;
+    for (int p = 0; p < 4; ++p) {
+        const int row = 16 * w + 4 * p + (lane >> 4);
+        const int ck = (lane & 15) ^ ((row ^ (row >> 3)) & 15);
+        d.k[p] = (4 * (p & 1) + (lane >> 4)) * 256 + ck * 16;
     }
+    d.v = lane * 16;
     return d;
 }
 
-// The next half block to fetch: destination stages, packed block j, half.
-struct DmaHalf {
-    uint32_t kst, vst;        // LDS byte addresses of this wave's first 1 KB segment of each stage
-    __amdgpu_buffer_rsrc_t rkp, rvt;
-    int j, half;
+// The chunk to fetch: destination stages (this wave's 4 KB share of each)
+// and the byte offsets, in the head's packed K and V copies, of this wave's
+// two groups.
+struct DmaChunk {
+    uint32_t kst, vst;
+    __amdgpu_buffer_rsrc_t rkp, rvg;
+    int sk[2], sv[2];
 };
 
 // One 1 KB LDS-DMA (16 bytes per lane), issued through inline assembly so
@@ -525,15 +528,16 @@ __device__ __forceinline__ void dma16(uint32_t m0v, int voff, int soff, __amdgpu
 #pragma clang diagnostic pop
 }
 
-__device__ __forceinline__ void dma_piece(const DmaHalf &d, const DmaLane &dl, int i) {
-    const int blk = d.j * kMaxSlots * 256;            // bytes of one packed block (K or V^T)
+// Piece i < 4: K rows 4i .. 4i + 3 of the wave's 16; i >= 4: V group
+// (i - 4) / 2, dd rows 64 ((i - 4) % 2) .. + 63.
+__device__ __forceinline__ void dma_piece(const DmaChunk &d, const DmaLane &dl, int i) {
     if (i < 4)
-        dma16(d.kst + i * 1024, dl.off[i], blk + d.half * (kHalf * 256), d.rkp);
+        dma16(d.kst + i * 1024, dl.k[i], d.sk[i >> 1], d.rkp);
     else
-        dma16(d.vst + (i - 4) * 1024, dl.off[i], blk + d.half * (kHalf * 2), d.rvt);
+        dma16(d.vst + (i - 4) * 1024, dl.v, d.sv[(i - 4) >> 1] + ((i - 4) & 1) * 1024, d.rvg);
 }
 
-__device__ __forceinline__ void dma_half(const DmaHalf &d, const DmaLane &dl) {
+__device__ __forceinline__ void dma_chunk(const DmaChunk &d, const DmaLane &dl) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) dma_piece(d, dl, i);
 }
@@ -541,11 +545,11 @@ __device__ __forceinline__ void dma_half(const DmaHalf &d, const DmaLane &dl) {
 // Per-lane LDS byte offsets of the MFMA operand reads, fixed for the whole
 // kernel.  K: the subtile t and the stage add immediates; the chunk order of
 // k-step s for subtile 1 is that of step s ^ 2 for subtile 0 (the swizzle of
-// row 32 + x is the swizzle of row x with bit 2 flipped).  V^T: the 32-row
-// tile u adds an immediate.
+// row 32 + x is the swizzle of row x with bit 2 flipped).  V: key step sg
+// reads group 2 sg + h, dd row 32 u + lane % 32 (u adds an immediate).
 struct OperandAddr {
     uint32_t k[8];    // K row krow(l32), chunk for k-step s, subtile 0
-    uint32_t v[4];    // V^T row l32, group for key step sg
+    uint32_t v[4];    // V group 2 sg + h, dd row l32
 };
 
 __device__ __forceinline__ OperandAddr operand_addr(int lane) {
@@ -555,7 +559,7 @@ __device__ __forceinline__ OperandAddr operand_addr(int lane) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) o.k[s] = (uint32_t)(krow * 256 + (kpos128(krow, 2 * s + h) << 4));
 #pragma unroll
-    for (int sg = 0; sg < 4; ++sg) o.v[sg] = (uint32_t)(l32 * kHalf * 2 + (vpos128(l32, 2 * sg + h) << 4));
+    for (int sg = 0; sg < 4; ++sg) o.v[sg] = (uint32_t)((2 * sg + h) * 2048 + l32 * 16);
     return o;
 }
 
@@ -563,15 +567,15 @@ __device__ __forceinline__ bf16x8 lds_read16(const uint16_t *base, uint32_t byte
     return *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const char *>(base) + byte_off);
 }
 
-// One 64-key half block for one wave's 32 queries; keys at or past nvalid get
-// zero probability.
-// The DMA of the next half block `dn` is issued one piece per k-step of
+// One 64-key chunk for one wave's 32 queries; keys whose bit is clear in the
+// 64-bit mask (mlo, mhi) get zero probability.
+// The DMA of the next chunk `dn` is issued one piece per k-step of
 // Q K^T, so the loads are spread over the MFMA stream instead of arriving in
 // one burst; the scheduling groups below keep six operand reads in flight
 // ahead of the MFMAs and put one DMA piece in each group.
-__device__ __forceinline__ void half_tile(const uint16_t *Kt, const uint16_t *Vt, int nvalid, const bf16x8 *qf,
-                                          f32x16 *acc, float &m_run, float &l_run, float c, int h,
-                                          const OperandAddr &oa, const DmaHalf &dn, const DmaLane &dl) {
+__device__ __forceinline__ void chunk_tile(const uint16_t *Kt, const uint16_t *Vt, uint32_t mlo, uint32_t mhi,
+                                          const bf16x8 *qf, f32x16 *acc, float &m_run, float &l_run, float c,
+                                          int h, const OperandAddr &oa, const DmaChunk &dn, const DmaLane &dl) {
     f32x16 sacc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -598,14 +602,16 @@ __device__ __forceinline__ void half_tile(const uint16_t *Kt, const uint16_t *Vt
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
-    if (nvalid < kHalf) {
-        // key 32t + 16(r/8) + 8h + r%8 is masked when it reaches nvalid
-        const int lim = nvalid - 8 * h;
+    if ((mlo & mhi) != 0xffffffffu) {
+        // key 32t + 16(r/8) + 8h + r%8 is masked unless its bit is set
+        // (bits 0-31 in mlo, 32-63 in mhi); this lane's bits are those of
+        // h = 0 shifted down by 8h
+        const uint32_t l0 = mlo >> (8 * h), l1 = mhi >> (8 * h);
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                if (32 * t + 16 * (r >> 3) + (r & 7) >= lim) sacc[t][r] = -INFINITY;
+                if (!(((t ? l1 : l0) >> (16 * (r >> 3) + (r & 7))) & 1u)) sacc[t][r] = -INFINITY;
     }
     bf16x8 pf[4];
     float hs = half_probs(sacc, c, m_run, pf);
@@ -635,7 +641,7 @@ __device__ __forceinline__ void half_tile(const uint16_t *Kt, const uint16_t *Vt
     for (int sg = 0; sg < 4; ++sg) {
         bf16x8 vf[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) vf[u] = lds_read16(Vt + u * 32 * kHalf, oa.v[sg]);
+        for (int u = 0; u < 4; ++u) vf[u] = lds_read16(Vt + u * 32 * 8, oa.v[sg]);
 #pragma unroll
         for (int u = 0; u < 4; ++u) acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u], pf[sg], acc[u], 0, 0, 0);
     }
@@ -645,10 +651,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
                                                                   const uint16_t *Vt_all) {
     // Two LDS stages as distinct objects, so the compiler can see that the
     // DMA into one stage does not alias the reads of the other.
-    __shared__ __attribute__((aligned(16))) uint16_t Ks0[kHalf * 128];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs0[kHalf * 128];
-    __shared__ __attribute__((aligned(16))) uint16_t Ks1[kHalf * 128];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs1[kHalf * 128];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks0[kChunk * 128];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs0[kChunk * 128];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks1[kChunk * 128];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs1[kChunk * 128];
     __shared__ int s_item;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
@@ -714,46 +720,95 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
         if (nkb > 0) {
             const int64_t head_packed = (int64_t)bh * g.Nb * kMaxSlots * 128;
             const __amdgpu_buffer_rsrc_t rkp = head_rsrc(Kp_all + head_packed, (int64_t)g.Nb * kMaxSlots * 256);
-            const __amdgpu_buffer_rsrc_t rvt = head_rsrc(Vt_all + head_packed, (int64_t)g.Nb * kMaxSlots * 256);
+            const __amdgpu_buffer_rsrc_t rvg = head_rsrc(Vt_all + head_packed, (int64_t)g.Nb * kMaxSlots * 256);
             const cptr_i32 bsz = (cptr_i32)a.bsize;
-            // Half-block stream over the kept blocks: block jj (index j, nj
-            // tokens), half hh.  Block indices are read two blocks ahead and
-            // sizes one block ahead (scalar loads), K/V one half ahead (DMA).
-            int jj = 0, hh = 0;
-            int e0 = cols[0];
-            int j = e0 & 0xffff, nj = bsz[j];
-            bool own = mine(e0);
-            int e1 = (nkb > 1) ? cols[1] : 0;
-            int j1 = e1 & 0xffff;
-            int n1 = (nkb > 1) ? bsz[j1] : 0;
-            int e2 = (nkb > 2) ? cols[2] : 0;
             auto lds_addr = [](const uint16_t *p) { return (uint32_t)(uintptr_t)(const lds_ptr_t)p; };
-            dma_half(DmaHalf{lds_addr(Ks0) + seg0, lds_addr(Vs0) + seg0, rkp, rvt, j, 0}, dl);
-            // One step of the stream: wait for the current stage, start the
-            // DMA of the next half into the other stage, compute the current.
-            // Unrolled by two so both stages are fixed objects in each step.
-            auto step = [&](uint16_t *Kc, uint16_t *Vc, uint16_t *Kn, uint16_t *Vn) -> bool {
-                const bool same = (hh + 1) * kHalf < nj;
-                const int jn = same ? jj : jj + 1;
-                const int hn = same ? hh + 1 : 0;
-                const int jnext = same ? j : j1;
-                __builtin_amdgcn_s_waitcnt(0x0f70);       // vmcnt(0): this wave's DMA for the current half landed
-                __syncthreads();                          // ... and every wave's; the other stage is free again
-                // After the last half there is nothing to fetch: the DMA then
-                // reloads the current half into the free stage (harmless, and
-                // it keeps the k-step loop free of branches).
-                const bool more = jn < nkb;
-                const DmaHalf dn{lds_addr(Kn) + seg0, lds_addr(Vn) + seg0, rkp, rvt, more ? jnext : j, more ? hn : hh};
-                if (active && own) half_tile(Kc, Vc, nj - hh * kHalf, qf, acc, m_run, l_run, c, h, oa, dn, dl);
-                else dma_half(dn, dl);
-                if (jn >= nkb) return false;
-                if (!same) {
-                    jj = jn;
-                    j = j1; nj = n1; own = mine(e1);
-                    if (jj + 1 < nkb) { e1 = e2; j1 = e2 & 0xffff; n1 = bsz[j1]; }
-                    if (jj + 2 < nkb) e2 = cols[jj + 2];
+            // Chunk stream over the kept blocks.  Cursor: list position p,
+            // key offset o (a multiple of 8) in that block.  Block entries
+            // are read two positions ahead and sizes one ahead (scalar
+            // loads): e0/n0 at p, e1/n1 at p + 1, e2 at p + 2.
+            int p = 0, o = 0;
+            int e0 = cols[0], n0 = bsz[e0 & 0xffff];
+            int e1 = (nkb > 1) ? cols[1] : 0;
+            int n1 = (nkb > 1) ? bsz[e1 & 0xffff] : 0;
+            int e2 = (nkb > 2) ? cols[2] : 0;
+            // Describe the next chunk and advance the cursor past it: this
+            // wave's two group sources (block 0 of the head for groups past
+            // the end: valid memory, masked keys) and this wave pair's key
+            // mask (valid, owned keys).  Returns false when the stream ended.
+            auto advance = [&]() {
+                ++p;
+                o = 0;
+                e0 = e1; n0 = n1;
+                if (p + 1 < nkb) { e1 = e2; n1 = bsz[e2 & 0xffff]; }
+                if (p + 2 < nkb) e2 = cols[p + 2];
+            };
+            auto walk = [&](DmaChunk &d, uint32_t &mlo, uint32_t &mhi) -> bool {
+                d.sk[0] = d.sk[1] = d.sv[0] = d.sv[1] = 0;
+                mlo = mhi = 0u;
+                if (p >= nkb) return false;
+                if (o + kChunk <= n0) {
+                    // the common case: 64 valid keys of block p
+                    const int j = e0 & 0xffff;
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const int slot = o + 16 * wu + 8 * t;
+                        d.sk[t] = (j * kMaxSlots + slot) * 256;
+                        d.sv[t] = (j * 16 + (slot >> 3)) * 2048;
+                    }
+                    mlo = mhi = mine(e0) ? 0xffffffffu : 0u;
+                    o += kChunk;
+                    if (o >= ((n0 + 7) & ~7)) advance();
+                    return true;
                 }
-                hh = hn;
+                int x0 = 0;
+                while (x0 < kChunk && p < nkb) {
+                    const int j = e0 & 0xffff;
+                    const int n8 = (n0 + 7) & ~7;
+                    const int L = min(n8 - o, kChunk - x0);
+                    const int nv = min(L, n0 - o);
+                    if (mine(e0)) {
+                        const uint64_t bits = (nv >= 64 ? ~0ull : ((1ull << nv) - 1ull)) << x0;
+                        mlo |= (uint32_t)bits;
+                        mhi |= (uint32_t)(bits >> 32);
+                    }
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const int xg = 16 * wu + 8 * t;        // this wave's group t within the chunk
+                        if (xg >= x0 && xg < x0 + L) {
+                            const int slot = o + xg - x0;
+                            d.sk[t] = (j * kMaxSlots + slot) * 256;
+                            d.sv[t] = (j * 16 + (slot >> 3)) * 2048;
+                        }
+                    }
+                    x0 += L;
+                    o += L;
+                    if (o >= n8) advance();
+                }
+                return true;
+            };
+            DmaChunk dc, dn;
+            uint32_t cl, ch, nl, nh;
+            walk(dc, cl, ch);
+            dc.kst = lds_addr(Ks0) + seg0; dc.vst = lds_addr(Vs0) + seg0; dc.rkp = rkp; dc.rvg = rvg;
+            dma_chunk(dc, dl);
+            bool more = walk(dn, nl, nh);
+            // One step of the stream: wait for the current stage, start the
+            // DMA of the next chunk into the other stage, compute the
+            // current one, describe the chunk after.  Unrolled by two so both
+            // stages are fixed objects in each step.  After the last chunk
+            // the DMA reloads the current one into the free stage (harmless,
+            // and it keeps the k-step loop free of branches).
+            auto step = [&](uint16_t *Kc, uint16_t *Vc, uint16_t *Kn, uint16_t *Vn) -> bool {
+                __builtin_amdgcn_s_waitcnt(0x0f70);       // vmcnt(0): this wave's DMA for the current chunk landed
+                __syncthreads();                          // ... and every wave's; the other stage is free again
+                DmaChunk df = more ? dn : dc;
+                df.kst = lds_addr(Kn) + seg0; df.vst = lds_addr(Vn) + seg0; df.rkp = rkp; df.rvg = rvg;
+                if (active && (cl | ch)) chunk_tile(Kc, Vc, cl, ch, qf, acc, m_run, l_run, c, h, oa, df, dl);
+                else dma_chunk(df, dl);
+                if (!more) return false;
+                dc = dn; cl = nl; ch = nh;
+                more = walk(dn, nl, nh);
                 return true;
             };
             while (step(Ks0, Vs0, Ks1, Vs1) && step(Ks1, Vs1, Ks0, Vs0)) {
@@ -800,11 +855,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
 }
 
 // Block-major copies for the d=128 kernel, one workgroup per (block,
-// batch*head): Kp[(bh*Nb + j)*128 + slot][128] and Vt[(bh*Nb + j)*128 + dd][128
-// slots], slots past the block's tokens zero.  K: 16 lanes move one 256-byte
-// row.  V: each thread transposes an 8x8 tile (8 slots of one 16-byte chunk)
-// in registers, with the threads of a wave on 4 chunks x all 16 slot groups,
-// so that every V^T store of a wave fills whole rows.
+// batch*head): Kp[(bh*Nb + j)*128 + slot][128] and, per 8-slot group g,
+// Vg[((bh*Nb + j)*16 + g)*128 + dd][8 slots] (V^T of the group, 2 KB
+// contiguous), slots past the block's tokens zero.  K: 16 lanes move one
+// 256-byte row.  V: each thread transposes an 8x8 tile (8 slots of one
+// 16-byte chunk of the head dimension) in registers and writes its 128
+// contiguous bytes of the group.
 __global__ __launch_bounds__(256) void pack_kv_kernel(Geo g, const uint16_t *K, const uint16_t *V,
                                                       uint16_t *Kp, uint16_t *Vt) {
     const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
@@ -820,8 +876,7 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(Geo g, const uint16_t *K, 
         kx[m] = *reinterpret_cast<const u32x4 *>(K + hoff + (int64_t)bt.token(slot) * g.sn + c16 * 8);
     }
     // V: slots 8*hv .. 8*hv+7 of the 16-byte chunk cv, transposed in
-    // registers to 8 dd rows x 8 slots; a wave covers 4 chunks x 16 slot
-    // groups, so each of its stores fills whole 256-byte V^T rows.
+    // registers to 8 dd rows x 8 slots: dd rows 8cv .. 8cv+7 of group hv.
     const int hv = tid & 15, cv = tid >> 4;
     u32x4 in[8];
 #pragma unroll
@@ -845,7 +900,88 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(Geo g, const uint16_t *K, 
         u32x4 o;
 #pragma unroll
         for (int w = 0; w < 4; ++w) o[w] = __builtin_amdgcn_perm(in[2 * w + 1][e >> 1], in[2 * w][e >> 1], sel);
-        *reinterpret_cast<u32x4 *>(Vt + pblk + dd * kMaxSlots + 8 * hv) = o;
+        *reinterpret_cast<u32x4 *>(Vt + pblk + (hv * 128 + dd) * 8) = o;
+    }
+}
+
+// The layer's prologue for bf16, d = 128, one workgroup per (block,
+// batch*head): the float64 means of Q and K over the block's tokens (the
+// pooling of the routing front end) and the block-major K and group-major V^T
+// copies of pack_kv_kernel, from a single read of each tensor.  The means are
+// summed in the order of the routing's own pooling (thread (c, g) adds rows
+// g, g + 16, ... of 16-byte chunk c, then the 16 row groups in order), so
+// they are bit for bit the same.
+__device__ __forceinline__ void add_rows_f64(double *acc, const u32x4 *x, int hi, int n) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        if (hi + 16 * m < n) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i] += (double)__uint_as_float(x[m][i] << 16);
+                acc[2 * i + 1] += (double)__uint_as_float(x[m][i] & 0xffff0000u);
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void reduce_mean(double *red, const double *acc, int c16, int hi, int n, double *out) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[hi * 128 + c16 * 8 + e] = acc[e];
+    __syncthreads();
+    if (threadIdx.x < 128) {
+        double sum = 0.0;
+        for (int q = 0; q < 16; ++q) sum += red[q * 128 + threadIdx.x];
+        out[threadIdx.x] = sum / (double)n;
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void prologue_kernel(Geo g, const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                                                       double *qbar, double *kbar, uint16_t *Kp, uint16_t *Vt) {
+    __shared__ double red[16 * 128];
+    const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+    const BlockTokens bt = block_tokens(g, j);
+    const int n = bt.n;
+    const int64_t hoff = (int64_t)(bh / g.H) * g.sb + (int64_t)(bh % g.H) * g.sh;
+    const int64_t pblk = ((int64_t)bh * g.Nb + j) * kMaxSlots * 128;
+    const int c16 = tid & 15, hi = tid >> 4;
+    const int hv = tid & 15, cv = tid >> 4;
+    u32x4 qx[8], kx[8], in[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const int64_t row = hoff + (int64_t)bt.token(hi + 16 * m) * g.sn + c16 * 8;
+        qx[m] = *reinterpret_cast<const u32x4 *>(Q + row);
+        kx[m] = *reinterpret_cast<const u32x4 *>(K + row);
+    }
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8)
+        in[s8] = *reinterpret_cast<const u32x4 *>(V + hoff + (int64_t)bt.token(8 * hv + s8) * g.sn + cv * 8);
+    double acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+    add_rows_f64(acc, qx, hi, n);
+    reduce_mean(red, acc, c16, hi, n, qbar + ((int64_t)bh * g.Nb + j) * 128);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+    add_rows_f64(acc, kx, hi, n);
+    reduce_mean(red, acc, c16, hi, n, kbar + ((int64_t)bh * g.Nb + j) * 128);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const int slot = hi + 16 * m;
+        if (slot >= n) kx[m] = u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4 *>(Kp + pblk + slot * 128 + c16 * 8) = kx[m];
+    }
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8)
+        if (8 * hv + s8 >= n) in[s8] = u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int dd = 8 * cv + e;
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        u32x4 o;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) o[w] = __builtin_amdgcn_perm(in[2 * w + 1][e >> 1], in[2 * w][e >> 1], sel);
+        *reinterpret_cast<u32x4 *>(Vt + pblk + (hv * 128 + dd) * 8) = o;
     }
 }
 
@@ -1395,6 +1531,14 @@ hipError_t launch_attention(const Geo &g, const void *q, const void *k, const vo
     if (e != hipSuccess) return e;
     if (ev1) e = hipEventRecord(ev1, s);
     return e;
+}
+
+hipError_t launch_prologue(const Geo &g, const void *q, const void *k, const void *v, double *qbar, double *kbar,
+                           uint16_t *kp, uint16_t *vt, hipStream_t s) {
+    if (!uses_packed_kv(g) || g.BH == 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(prologue_kernel, dim3(g.Nb, g.BH), dim3(256), 0, s, g, (const uint16_t *)q,
+                       (const uint16_t *)k, (const uint16_t *)v, qbar, kbar, kp, vt);
+    return hipGetLastError();
 }
 
 hipError_t launch_combine(const Geo &g, void *o, const int32_t *tok, const int32_t *bsize, const PlanHeader *hdr,

@@ -130,6 +130,8 @@ hipError_t launch_attention(const Geo &g, const void *q, const void *k, const vo
 size_t packed_kv_bytes(const Geo &g);
 bool uses_packed_kv(const Geo &g);
 hipError_t launch_pack_kv(const Geo &g, const void *k, const void *v, uint16_t *kp, uint16_t *vt, hipStream_t s);
+hipError_t launch_prologue(const Geo &g, const void *q, const void *k, const void *v, double *qbar, double *kbar,
+                           uint16_t *kp, uint16_t *vt, hipStream_t s);
 hipError_t launch_combine(const Geo &g, void *o, const int32_t *tok, const int32_t *bsize,
                           const PlanHeader *hdr, const SplitRow *splits, const float *part_o,
                           const float *part_ml, int cap_splits, hipStream_t s);

@@ -267,8 +267,9 @@ size_t fva_attn_stats_bytes(const fva_problem *prob, const fva_attn_options *opt
  * neighbouring query blocks of one head that each hold at most 64 tokens
  * (edge tiles) run as one work item over the union of their key lists, each
  * block attending only to its own kept blocks, in ascending block order; such
- * items are never split.  The results are those of the unpaired run (bit for
- * bit when the columns are ascending).
+ * items are never split.  The results are those of the unpaired run up to
+ * the rounding of the probabilities to bf16, which each run does against its
+ * own softmax offsets.
  */
 fva_status fva_sparse_attn(const fva_problem *prob, const void *q, const void *k, const void *v,
                            const fva_lists *lists, void *o, void *ws, size_t ws_bytes, void *stats,
@@ -292,6 +293,29 @@ fva_status fva_sparse_attn(const fva_problem *prob, const void *q, const void *k
  */
 fva_status fva_attn_prepare(const fva_problem *prob, const void *k, const void *v, void *ws, size_t ws_bytes,
                             const fva_attn_options *opts, void *stream);
+
+/* Workspace bytes fva_layer needs for these options (NULL = defaults): the
+ * routing workspace followed by the attention workspace (0 if the problem or
+ * options are invalid). */
+size_t fva_layer_workspace_bytes(const fva_problem *prob, const fva_attn_options *opts);
+
+/*
+ * One attention layer's whole hot path in one call: fva_route into `lists`,
+ * then fva_sparse_attn on those lists into `o`, on `stream`, with the
+ * arguments, checks and results of the two calls (paperlayer.ai summary of
+ * FVAttn, section 3 "FVAttn Design", Pipeline: routing, then sparse
+ * attention on the routed blocks).  For bf16 and head_dim 128 the two share
+ * one prologue kernel that reads each of Q, K and V once, for the routing's
+ * pooled block means and the attention's block-major K/V copies; lists and
+ * output are bit for bit those of the separate calls.  ws: device, at least
+ * fva_layer_workspace_bytes(prob, opts) bytes, 256-byte aligned.
+ * opts->flags must not hold FVA_ATTN_PREPARED; kernel_events, when given,
+ * bracket the attention kernel as in fva_sparse_attn.  budget: host pointer
+ * (the slack budget of fva_route; passed by address in this call).
+ */
+fva_status fva_layer(const fva_problem *prob, const void *q, const void *k, const void *v, double p, int32_t kmin,
+                     const fva_budget *budget, const fva_lists *lists, void *o, void *ws, size_t ws_bytes,
+                     void *stats, const fva_attn_options *opts, void *stream);
 
 /* Static string naming a status code. */
 const char *fva_status_string(fva_status s);

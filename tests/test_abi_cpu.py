@@ -327,3 +327,27 @@ def test_per_cu_imbalance_of_synthetic_records():
     half = [rec(0, c, 0, 100) for c in range(8)]                              # 8 of 16 CUs busy
     imb, _ = per_cu_imbalance(half, n)
     assert imb == 2.0
+
+
+def test_layer_checks_arguments_before_launching(lib):
+    """fva_layer's host checks (those of fva_route and fva_sparse_attn plus
+    its own) reject bad arguments before any launch; the budget is passed by
+    address."""
+    p = prob(heads=2, stride_b=2 * 75600 * 128)
+    fake = 1 << 20                                   # aligned, never dereferenced
+    lists = ListsC(fake, fake, None, None, None)
+    opts = fva.attn_options(num_ctas=512)            # no device query
+    wsb = lib.fva_layer_workspace_bytes(ctypes.byref(p), ctypes.byref(opts))
+    assert wsb >= lib.fva_route_workspace_bytes(ctypes.byref(p))
+    b = Budget(1, 0.1)
+
+    def call(pp=0.9, budget=ctypes.byref(b), o=fake, ws=fake * 256, nbytes=wsb, op=opts):
+        return lib.fva_layer(ctypes.byref(p), fake, fake, fake, pp, 8, budget, ctypes.byref(lists), o, ws, nbytes,
+                             None, ctypes.byref(op), None)
+
+    assert call(pp=0.0) == FVA_ERR_INVALID_ARG
+    assert call(budget=None) == FVA_ERR_INVALID_ARG
+    assert call(o=fake + 8) == FVA_ERR_INVALID_ARG
+    assert call(nbytes=wsb - 1) == FVA_ERR_WORKSPACE
+    prep = fva.attn_options(num_ctas=512, prepared=True)
+    assert call(op=prep) == FVA_ERR_INVALID_ARG
