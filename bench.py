@@ -1,14 +1,17 @@
 """Benchmark of the FVAttn block-sparse attention hot path on one MI355X.
 
-One step = the whole path on one synthetic layer: fva_route (pool, block
-scores, Top-p + floor, slack augmentation, CSR) then fva_sparse_attn (plan,
+One step = the whole path on one synthetic layer, as one fva_layer call:
+a prologue that reads Q, K and V once (pooled block means for the routing,
+the attention's packed K/V copies), the routing (block scores, Top-p +
+floor, slack augmentation, CSR lists), then the attention (plan,
 block-sparse flash attention, combine), with the inputs already resident in
-HBM.  The list-independent K/V copies (fva_attn_prepare) run on a second
-stream while the routing runs, joined before the attention.  The step is
-timed eagerly (ms_per_layer, `value`), then captured once in a HIP graph
-and timed as replays (ms_per_layer_graph; graph_replay_bit_exact says
-whether a replay reproduced the eager lists and output bit for bit).  The
-same step on one stream is timed too (ms_per_layer_one_stream).
+HBM.  The step is timed eagerly (ms_per_layer, `value`), then captured once
+in a HIP graph and timed as replays (ms_per_layer_graph;
+graph_replay_bit_exact says whether a replay reproduced the eager lists and
+output bit for bit).  For comparison the same work is timed as two calls:
+fva_route then fva_sparse_attn on one stream (ms_per_layer_one_stream), and
+with the K/V copies (fva_attn_prepare) on a second stream beside the
+routing (ms_per_layer_two_calls_overlapped).
 
 Workload (default): the 720p-shaped DiT self-attention layer - B=1, 40 heads,
 d=128, bf16, 21x45x80 latent tokens in 2x8x8 tiles, p=0.9, floor 8, +10%
@@ -181,26 +184,25 @@ def run_workload(w, args, q, k, v, hilbert, full):
     side = torch.cuda.Stream(dev)          # default priority, like the main stream
 
     def step(ev=None):
-        # K/V copies on the side stream (into the main stream's workspace)
-        # once the last attention has released it; routing meanwhile on the
-        # main stream; join, attend.
-        side.wait_stream(main)
-        with torch.cuda.stream(side):
-            if ev:
-                ev[5].record()
-            fva.attn_prepare(kd, vd, **blk, stream=main)
-            if ev:
-                ev[6].record()
+        # One call: prologue, routing and attention on the main stream.  The
+        # library records ev[3] / ev[4] right around the attention kernel.
         if ev:
             ev[0].record()
-        fva.route(qd, kd, w.p, w.kmin, w.budget, **blk, out=lists)
-        if ev:
-            ev[1].record()
-        main.wait_stream(side)
-        fva.sparse_attn(qd, kd, vd, lists, out=out, prepared=True,
-                        kernel_events=(ev[3], ev[4]) if ev else None)
+        fva.layer(qd, kd, vd, w.p, w.kmin, w.budget, **blk, lists=lists, out=out,
+                  kernel_events=(ev[3], ev[4]) if ev else None)
         if ev:
             ev[2].record()
+
+    def step_overlapped():
+        # Two calls, K/V copies on the side stream (into the main stream's
+        # workspace) once the last attention has released it, routing
+        # meanwhile on the main stream; join, attend.
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            fva.attn_prepare(kd, vd, **blk, stream=main)
+        fva.route(qd, kd, w.p, w.kmin, w.budget, **blk, out=lists)
+        main.wait_stream(side)
+        fva.sparse_attn(qd, kd, vd, lists, out=out, prepared=True)
 
     def step_one_stream():
         fva.route(qd, kd, w.p, w.kmin, w.budget, **blk, out=lists)
@@ -210,13 +212,14 @@ def run_workload(w, args, q, k, v, hilbert, full):
     for _ in range(args.warmup):
         step()
         if full:
+            step_overlapped()
             step_one_stream()
     torch.cuda.synchronize()
-    # Per step: events around the routing call and the attention call (main
-    # stream, where the library launches), the pair the library records right
-    # around the attention kernel proper, and a pair around the K/V copies on
-    # the side stream.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    # Per step: events around the call (main stream, where the library
+    # launches) and the pair the library records right around the attention
+    # kernel proper; what precedes that kernel is the prologue, the routing
+    # and the plan.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     for e in ev:                      # create the kernel events before the timed region
         e[3].record()
         e[4].record()
@@ -229,19 +232,25 @@ def run_workload(w, args, q, k, v, hilbert, full):
     stop.record()
     torch.cuda.synchronize()
     res = dict(ms_step=start.elapsed_time(stop) / args.steps,
-               route_ms=float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
-               attn_ms=float(np.mean([e[1].elapsed_time(e[2]) for e in ev])),
-               kernel_ms=float(np.mean([e[3].elapsed_time(e[4]) for e in ev])),
-               prepare_ms=float(np.mean([e[5].elapsed_time(e[6]) for e in ev])))
+               route_ms=float(np.mean([e[0].elapsed_time(e[3]) for e in ev])),
+               attn_ms=float(np.mean([e[3].elapsed_time(e[2]) for e in ev])),
+               kernel_ms=float(np.mean([e[3].elapsed_time(e[4]) for e in ev])))
     if full:
-        # The same step on one stream (everything in order), for comparison.
+        # The same work as two calls, overlapped and on one stream.
+        start.record()
+        for s in range(args.steps):
+            step_overlapped()
+        stop.record()
+        torch.cuda.synchronize()
+        res["ms_overlapped"] = start.elapsed_time(stop) / args.steps
         start.record()
         for s in range(args.steps):
             step_one_stream()
         stop.record()
         torch.cuda.synchronize()
         res["ms_one_stream"] = start.elapsed_time(stop) / args.steps
-        # The overlapped step captured once in a HIP graph and replayed.
+        # The step captured once in a HIP graph and replayed; one eager call
+        # on the capture stream first gives that stream its workspace.
         step()
         torch.cuda.synchronize()
         eager_o, eager_rp = out.clone(), lists.row_ptr.clone()
@@ -249,10 +258,11 @@ def run_workload(w, args, q, k, v, hilbert, full):
         cap = torch.cuda.Stream(dev)
         cap.wait_stream(main)
         with torch.cuda.stream(cap):
+            step()
+        cap.synchronize()
+        with torch.cuda.stream(cap):
             with torch.cuda.graph(graph, stream=cap):
-                main = torch.cuda.current_stream(dev)
                 step()
-        main = torch.cuda.current_stream(dev)
         main.wait_stream(cap)
         torch.cuda.synchronize()
         out.zero_()
@@ -269,7 +279,8 @@ def run_workload(w, args, q, k, v, hilbert, full):
         torch.cuda.synchronize()
         res["ms_graph"] = start.elapsed_time(stop) / args.steps
         del graph
-        log(f"[bench] {w.name}: eager {res['ms_step']:.3f} ms, one stream {res['ms_one_stream']:.3f} ms, "
+        log(f"[bench] {w.name}: eager {res['ms_step']:.3f} ms, two calls {res['ms_overlapped']:.3f} ms "
+            f"overlapped / {res['ms_one_stream']:.3f} ms one stream, "
             f"graph {res['ms_graph']:.3f} ms (replay {'matches' if res['graph_ok'] else 'DIFFERS FROM'} eager)")
     else:
         log(f"[bench] {w.name}: eager {res['ms_step']:.3f} ms")
@@ -373,9 +384,9 @@ def main():
         "ms_per_layer": round(ms_step, 4),
         "ms_per_layer_graph": round(r["ms_graph"], 4),
         "graph_replay_bit_exact": r["graph_ok"],
+        "ms_per_layer_two_calls_overlapped": round(r["ms_overlapped"], 4),
         "ms_per_layer_one_stream": round(r["ms_one_stream"], 4),
-        "route_ms": round(r["route_ms"], 4),
-        "attn_prepare_ms_side_stream": round(r["prepare_ms"], 4),
+        "pre_attn_ms": round(r["route_ms"], 4),
         "attn_ms": round(r["attn_ms"], 4),
         "attn_kernel_ms": round(kernel_ms, 4),
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
@@ -431,7 +442,7 @@ def main():
             "shard_ms_per_layer": round(rs["ms_step"], 4),
             "shard_tflops": round(sflops / (rs["ms_step"] * 1e-3) / 1e12, 2),
             "shard_attn_kernel_ms": round(rs["kernel_ms"], 4),
-            "shard_route_ms": round(rs["route_ms"], 4),
+            "shard_pre_attn_ms": round(rs["route_ms"], 4),
             "shard_per_cu_imbalance": round(rs["imbalance"], 4),
             "shard_per_workgroup_imbalance_predicted": round(float(rs["info"].predicted_imbalance), 4),
             "shard_block_density_per_head": [round(float(x), 4) for x in rs["density_per_head"]],

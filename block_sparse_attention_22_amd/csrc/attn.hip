@@ -602,6 +602,11 @@ __device__ __forceinline__ void chunk_tile(const uint16_t *Kt, const uint16_t *V
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
+    // The V operands of the first key step, read now so that their LDS
+    // latency passes during the softmax.
+    bf16x8 vf[2][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) vf[0][u] = lds_read16(Vt + u * 32 * 8, oa.v[0]);
     if ((mlo & mhi) != 0xffffffffu) {
         // key 32t + 16(r/8) + 8h + r%8 is masked unless its bit is set
         // (bits 0-31 in mlo, 32-63 in mhi); this lane's bits are those of
@@ -637,14 +642,28 @@ __device__ __forceinline__ void chunk_tile(const uint16_t *Kt, const uint16_t *V
         hs = half_probs(sacc, c, m_run, pf);
     }
     l_run += hs;
+    // P V, the operands of key step sg + 1 read while step sg multiplies
+    // (two register sets, so no read waits for an MFMA to release its
+    // registers).
 #pragma unroll
     for (int sg = 0; sg < 4; ++sg) {
-        bf16x8 vf[4];
+        if (sg < 3) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) vf[u] = lds_read16(Vt + u * 32 * 8, oa.v[sg]);
+            for (int u = 0; u < 4; ++u) vf[(sg + 1) & 1][u] = lds_read16(Vt + u * 32 * 8, oa.v[sg + 1]);
+        }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u], pf[sg], acc[u], 0, 0, 0);
+        for (int u = 0; u < 4; ++u)
+            acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[sg & 1][u], pf[sg], acc[u], 0, 0, 0);
     }
+    // masks: 0x100 LDS read, 0x008 MFMA
+#pragma unroll
+    for (int sg = 0; sg < 3; ++sg)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
 __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, const uint16_t *Kp_all,
@@ -857,60 +876,74 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
 // Block-major copies for the d=128 kernel, one workgroup per (block,
 // batch*head): Kp[(bh*Nb + j)*128 + slot][128] and, per 8-slot group g,
 // Vg[((bh*Nb + j)*16 + g)*128 + dd][8 slots] (V^T of the group, 2 KB
-// contiguous), slots past the block's tokens zero.  K: 16 lanes move one
-// 256-byte row.  V: each thread transposes an 8x8 tile (8 slots of one
-// 16-byte chunk of the head dimension) in registers and writes its 128
-// contiguous bytes of the group.
+// contiguous), slots past the block's tokens zero.  Every global access is
+// a 256-byte row moved by 16 lanes (K, V reads; K writes) or 16-byte
+// chunks consecutive across lanes (V^T writes): V goes through LDS, where
+// thread t builds chunks t, t + 256, ... of the block's V^T from eight
+// 2-byte reads of one column each (the 64 lanes of a wave read 64
+// consecutive columns of one row: no bank conflicts).
+__device__ __forceinline__ void load_rows(u32x4 *x, const uint16_t *T, const BlockTokens &bt, int64_t hoff,
+                                          int64_t sn, int c16, int hi) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+        x[m] = *reinterpret_cast<const u32x4 *>(T + hoff + (int64_t)bt.token(hi + 16 * m) * sn + c16 * 8);
+}
+
+__device__ __forceinline__ void stage_rows(uint16_t *vs, const u32x4 *x, int c16, int hi) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) *reinterpret_cast<u32x4 *>(vs + (hi + 16 * m) * 128 + c16 * 8) = x[m];
+}
+
+__device__ __forceinline__ void write_k_rows(uint16_t *Kp_blk, u32x4 *x, int n, int c16, int hi) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const int slot = hi + 16 * m;
+        if (slot >= n) x[m] = u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4 *>(Kp_blk + slot * 128 + c16 * 8) = x[m];
+    }
+}
+
+// After a barrier behind stage_rows: the block's V^T chunks from LDS.
+__device__ __forceinline__ void write_vt_groups(uint16_t *Vt_blk, const uint16_t *vs, int n) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int c = threadIdx.x + 256 * i;          // chunk (g, dd) = (c / 128, c % 128)
+        const int r0 = 8 * (c >> 7), dd = c & 127;
+        u32x4 o;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t lo = (r0 + 2 * w < n) ? vs[(r0 + 2 * w) * 128 + dd] : 0u;
+            const uint32_t hi = (r0 + 2 * w + 1 < n) ? vs[(r0 + 2 * w + 1) * 128 + dd] : 0u;
+            o[w] = lo | (hi << 16);
+        }
+        *reinterpret_cast<u32x4 *>(Vt_blk + c * 8) = o;
+    }
+}
+
 __global__ __launch_bounds__(256) void pack_kv_kernel(Geo g, const uint16_t *K, const uint16_t *V,
                                                       uint16_t *Kp, uint16_t *Vt) {
+    __shared__ __attribute__((aligned(16))) uint16_t vs[kMaxSlots * 128];
     const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
     const BlockTokens bt = block_tokens(g, j);
     const int64_t hoff = (int64_t)(bh / g.H) * g.sb + (int64_t)(bh % g.H) * g.sh;
     const int64_t pblk = ((int64_t)bh * g.Nb + j) * kMaxSlots * 128;
     const int c16 = tid & 15, hi = tid >> 4;
-    // K: 16 lanes move one 256-byte row (coalesced reads and writes).
-    u32x4 kx[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const int slot = hi + 16 * m;
-        kx[m] = *reinterpret_cast<const u32x4 *>(K + hoff + (int64_t)bt.token(slot) * g.sn + c16 * 8);
-    }
-    // V: slots 8*hv .. 8*hv+7 of the 16-byte chunk cv, transposed in
-    // registers to 8 dd rows x 8 slots: dd rows 8cv .. 8cv+7 of group hv.
-    const int hv = tid & 15, cv = tid >> 4;
-    u32x4 in[8];
-#pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) {
-        const int slot = 8 * hv + s8;
-        in[s8] = *reinterpret_cast<const u32x4 *>(V + hoff + (int64_t)bt.token(slot) * g.sn + cv * 8);
-    }
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const int slot = hi + 16 * m;
-        if (slot >= bt.n) kx[m] = u32x4{0, 0, 0, 0};
-        *reinterpret_cast<u32x4 *>(Kp + pblk + slot * 128 + c16 * 8) = kx[m];
-    }
-#pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8)
-        if (8 * hv + s8 >= bt.n) in[s8] = u32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int dd = 8 * cv + e;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        u32x4 o;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) o[w] = __builtin_amdgcn_perm(in[2 * w + 1][e >> 1], in[2 * w][e >> 1], sel);
-        *reinterpret_cast<u32x4 *>(Vt + pblk + (hv * 128 + dd) * 8) = o;
-    }
+    u32x4 kx[8], vx[8];
+    load_rows(kx, K, bt, hoff, g.sn, c16, hi);
+    load_rows(vx, V, bt, hoff, g.sn, c16, hi);
+    stage_rows(vs, vx, c16, hi);
+    write_k_rows(Kp + pblk, kx, bt.n, c16, hi);
+    __syncthreads();
+    write_vt_groups(Vt + pblk, vs, bt.n);
 }
 
 // The layer's prologue for bf16, d = 128, one workgroup per (block,
 // batch*head): the float64 means of Q and K over the block's tokens (the
-// pooling of the routing front end) and the block-major K and group-major V^T
-// copies of pack_kv_kernel, from a single read of each tensor.  The means are
-// summed in the order of the routing's own pooling (thread (c, g) adds rows
-// g, g + 16, ... of 16-byte chunk c, then the 16 row groups in order), so
-// they are bit for bit the same.
+// pooling of the routing front end) and the copies of pack_kv_kernel, from a
+// single read of each tensor.  The means are summed in the order of the
+// routing's own pooling (thread (c, g) adds rows g, g + 16, ... of 16-byte
+// chunk c, then the 16 row groups in order), so they are bit for bit the
+// same.
 __device__ __forceinline__ void add_rows_f64(double *acc, const u32x4 *x, int hi, int n) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
@@ -939,50 +972,29 @@ __device__ __forceinline__ void reduce_mean(double *red, const double *acc, int 
 __global__ __launch_bounds__(256) void prologue_kernel(Geo g, const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                                                        double *qbar, double *kbar, uint16_t *Kp, uint16_t *Vt) {
     __shared__ double red[16 * 128];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[kMaxSlots * 128];
     const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
     const BlockTokens bt = block_tokens(g, j);
     const int n = bt.n;
     const int64_t hoff = (int64_t)(bh / g.H) * g.sb + (int64_t)(bh % g.H) * g.sh;
     const int64_t pblk = ((int64_t)bh * g.Nb + j) * kMaxSlots * 128;
     const int c16 = tid & 15, hi = tid >> 4;
-    const int hv = tid & 15, cv = tid >> 4;
-    u32x4 qx[8], kx[8], in[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const int64_t row = hoff + (int64_t)bt.token(hi + 16 * m) * g.sn + c16 * 8;
-        qx[m] = *reinterpret_cast<const u32x4 *>(Q + row);
-        kx[m] = *reinterpret_cast<const u32x4 *>(K + row);
-    }
-#pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8)
-        in[s8] = *reinterpret_cast<const u32x4 *>(V + hoff + (int64_t)bt.token(8 * hv + s8) * g.sn + cv * 8);
+    u32x4 qx[8], kx[8], vx[8];
+    load_rows(qx, Q, bt, hoff, g.sn, c16, hi);
+    load_rows(kx, K, bt, hoff, g.sn, c16, hi);
+    load_rows(vx, V, bt, hoff, g.sn, c16, hi);
+    stage_rows(vs, vx, c16, hi);
     double acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0;
     add_rows_f64(acc, qx, hi, n);
-    reduce_mean(red, acc, c16, hi, n, qbar + ((int64_t)bh * g.Nb + j) * 128);
+    reduce_mean(red, acc, c16, hi, n, qbar + ((int64_t)bh * g.Nb + j) * 128);   // its barriers publish vs
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0;
     add_rows_f64(acc, kx, hi, n);
     reduce_mean(red, acc, c16, hi, n, kbar + ((int64_t)bh * g.Nb + j) * 128);
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const int slot = hi + 16 * m;
-        if (slot >= n) kx[m] = u32x4{0, 0, 0, 0};
-        *reinterpret_cast<u32x4 *>(Kp + pblk + slot * 128 + c16 * 8) = kx[m];
-    }
-#pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8)
-        if (8 * hv + s8 >= n) in[s8] = u32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int dd = 8 * cv + e;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        u32x4 o;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) o[w] = __builtin_amdgcn_perm(in[2 * w + 1][e >> 1], in[2 * w][e >> 1], sel);
-        *reinterpret_cast<u32x4 *>(Vt + pblk + (hv * 128 + dd) * 8) = o;
-    }
+    write_k_rows(Kp + pblk, kx, n, c16, hi);
+    write_vt_groups(Vt + pblk, vs, n);
 }
 
 // Float32 path: one thread per query slot, K/V tiles of one key block in LDS.
