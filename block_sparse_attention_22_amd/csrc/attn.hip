@@ -589,24 +589,26 @@ __device__ __forceinline__ void chunk_tile(const uint16_t *Kt, const uint16_t *V
         sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], sacc[0], 0, 0, 0);
         sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], sacc[1], 0, 0, 0);
     }
-    // masks: 0x100 LDS read, 0x020 VMEM read, 0x008 MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-    for (int s = 0; s < 5; ++s) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    }
     // The V operands of the first key step, read now so that their LDS
     // latency passes during the softmax.
     bf16x8 vf[2][4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) vf[0][u] = lds_read16(Vt + u * 32 * 8, oa.v[0]);
+    // Scheduling groups (masks: 0x100 LDS read, 0x020 VMEM read, 0x008
+    // MFMA): ten K operand reads ahead of the first MFMA, then per pair of
+    // MFMAs one DMA piece and the next reads (the V reads in the last ones).
+    __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        else if (s < 7) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    // The softmax runs at raised wave priority: while one wave of a SIMD
+    // works through it, the other's MFMAs still fill the matrix core, and
+    // this wave's vector work is not held back behind them.
+    __builtin_amdgcn_s_setprio(1);
     if ((mlo & mhi) != 0xffffffffu) {
         // key 32t + 16(r/8) + 8h + r%8 is masked unless its bit is set
         // (bits 0-31 in mlo, 32-63 in mhi); this lane's bits are those of
@@ -642,6 +644,7 @@ __device__ __forceinline__ void chunk_tile(const uint16_t *Kt, const uint16_t *V
         hs = half_probs(sacc, c, m_run, pf);
     }
     l_run += hs;
+    __builtin_amdgcn_s_setprio(0);
     // P V, the operands of key step sg + 1 read while step sg multiplies
     // (two register sets, so no read waits for an MFMA to release its
     // registers).
