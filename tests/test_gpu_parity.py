@@ -750,6 +750,47 @@ def test_graph_capture_replays(dev):
         torch.cuda.synchronize()
 
 
+def test_layer_graph_capture_replays(dev):
+    """fva_layer captured in one HIP graph: every replay, with eager layer
+    calls on other inputs between them on the same workspace, reproduces the
+    eager lists and output bit for bit, at 720p (the 5-head shard) and at the
+    mid bf16 size."""
+    for cid in (4, 2):
+        w = WORKLOADS[cid]
+        q, k, v, _ = make_inputs(w)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        blk = dict(grid=w.grid, tile=w.tile)
+        lists, out = fva.layer(qd, kd, vd, w.p, w.kmin, w.budget, **blk)
+        torch.cuda.synchronize()
+        ref_o, ref_rp = out.clone(), lists.row_ptr.clone()
+        ref_ci = lists.col_idx[: int(ref_rp[-1].item())].clone()
+        q2, k2 = qd.flip(2).contiguous(), kd.flip(2).contiguous()
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream(dev)
+        cap.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(cap):
+            fva.layer(qd, kd, vd, w.p, w.kmin, w.budget, **blk, lists=lists, out=out)   # the stream's workspace
+        cap.synchronize()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                fva.layer(qd, kd, vd, w.p, w.kmin, w.budget, **blk, lists=lists, out=out)
+        torch.cuda.current_stream(dev).wait_stream(cap)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            out.zero_()
+            lists.row_ptr.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(lists.row_ptr, ref_rp), (cid, rep)
+            assert torch.equal(lists.col_idx[: ref_ci.numel()], ref_ci), (cid, rep)
+            assert torch.equal(out, ref_o), (cid, rep)
+            with torch.cuda.stream(cap):
+                fva.layer(q2, k2, vd, w.p, w.kmin, w.budget, **blk)
+            torch.cuda.synchronize()
+        del g
+        print(f"\n[graph] {w.name}: 3 replays of the layer bit-exact", flush=True)
+
+
 def test_two_streams_with_different_problems(dev):
     """Route + attention of two different problems issued on two streams with
     no ordering between them, small first and then large, three times: each
