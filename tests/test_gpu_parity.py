@@ -750,11 +750,13 @@ def test_graph_capture_replays(dev):
         torch.cuda.synchronize()
 
 
-def test_layer_graph_capture_replays(dev):
+def test_layer_graph_capture_replays(dev, tmp_path):
     """fva_layer captured in one HIP graph: every replay, with eager layer
     calls on other inputs between them on the same workspace, reproduces the
     eager lists and output bit for bit, at 720p (the 5-head shard) and at the
-    mid bf16 size."""
+    mid bf16 size; the replayed lists equal the oracle's and the replayed
+    output is within tolerance of the oracle (every query block of the mid
+    size, 64 seeded ones of the shard)."""
     for cid in (4, 2):
         w = WORKLOADS[cid]
         q, k, v, _ = make_inputs(w)
@@ -787,8 +789,27 @@ def test_layer_graph_capture_replays(dev):
             with torch.cuda.stream(cap):
                 fva.layer(q2, k2, vd, w.p, w.kmin, w.budget, **blk)
             torch.cuda.synchronize()
+        # the last replay against the oracle
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
         del g
-        print(f"\n[graph] {w.name}: 3 replays of the layer bit-exact", flush=True)
+        lay = BlockLayout(w.grid, w.tile)
+        gl = gpu_lists_to_host(lists)
+        ref = routing.route(to_numpy(q), to_numpy(k), lay, w.p, w.kmin, w.budget)
+        rep = compare_lists(gl, ref, w.p, w.budget, lay, w.B, w.H)
+        assert_exact(rep)
+        nb = lay.Nb
+        if cid == 2:
+            rows = [(bh, i) for bh in range(w.B * w.H) for i in range(nb)]
+        else:
+            pick = np.random.default_rng(160).choice(w.B * w.H * nb, 64, replace=False)
+            rows = [(int(x) // nb, int(x) % nb) for x in np.sort(pick)]
+        errs, _ = _oracle_errors(tmp_path, cid, lay, q, k, v, out, gl, rows)
+        err = float(errs.max())
+        print(f"\n[graph] {w.name}: 3 replays of the layer bit-exact; replayed lists exact, "
+              f"max|o - oracle| = {err:.3e} on {len(rows)} query blocks", flush=True)
+        assert err <= TOL["bf16"]
 
 
 def test_two_streams_with_different_problems(dev):
