@@ -658,6 +658,9 @@ def test_empty_problem(dev):
     assert lists.row_ptr.cpu().tolist() == [0]
     o = fva.sparse_attn(q, q, q, lists)
     assert o.shape == q.shape
+    l2, o2 = fva.layer(q, q, q, 0.9, 1, None, grid=(4, 8, 8), tile=(1, 8, 8))
+    torch.cuda.synchronize()
+    assert l2.row_ptr.cpu().tolist() == [0] and o2.shape == q.shape
 
 
 def test_stats_and_per_cu_imbalance(dev):
