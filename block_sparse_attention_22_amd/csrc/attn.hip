@@ -972,10 +972,14 @@ __device__ __forceinline__ void reduce_mean(double *red, const double *acc, int 
     __syncthreads();
 }
 
-__global__ __launch_bounds__(256) void prologue_kernel(Geo g, const uint16_t *Q, const uint16_t *K, const uint16_t *V,
-                                                       double *qbar, double *kbar, uint16_t *Kp, uint16_t *Vt) {
-    __shared__ double red[16 * 128];
+// 32 KB of LDS and at most 128 registers, so that four workgroups share a
+// compute unit: the V^T staging area holds the two reductions' partial sums
+// first (16 KB), then V.
+__global__ __launch_bounds__(256, 4) void prologue_kernel(Geo g, const uint16_t *Q, const uint16_t *K,
+                                                          const uint16_t *V, double *qbar, double *kbar, uint16_t *Kp,
+                                                          uint16_t *Vt) {
     __shared__ __attribute__((aligned(16))) uint16_t vs[kMaxSlots * 128];
+    double *red = reinterpret_cast<double *>(vs);
     const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
     const BlockTokens bt = block_tokens(g, j);
     const int n = bt.n;
@@ -986,17 +990,18 @@ __global__ __launch_bounds__(256) void prologue_kernel(Geo g, const uint16_t *Q,
     load_rows(qx, Q, bt, hoff, g.sn, c16, hi);
     load_rows(kx, K, bt, hoff, g.sn, c16, hi);
     load_rows(vx, V, bt, hoff, g.sn, c16, hi);
-    stage_rows(vs, vx, c16, hi);
     double acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0;
     add_rows_f64(acc, qx, hi, n);
-    reduce_mean(red, acc, c16, hi, n, qbar + ((int64_t)bh * g.Nb + j) * 128);   // its barriers publish vs
+    reduce_mean(red, acc, c16, hi, n, qbar + ((int64_t)bh * g.Nb + j) * 128);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0;
     add_rows_f64(acc, kx, hi, n);
-    reduce_mean(red, acc, c16, hi, n, kbar + ((int64_t)bh * g.Nb + j) * 128);
+    reduce_mean(red, acc, c16, hi, n, kbar + ((int64_t)bh * g.Nb + j) * 128);   // ends with a barrier: red is free
+    stage_rows(vs, vx, c16, hi);
     write_k_rows(Kp + pblk, kx, n, c16, hi);
+    __syncthreads();
     write_vt_groups(Vt + pblk, vs, n);
 }
 
@@ -1240,6 +1245,11 @@ __device__ inline void plan_scan4(int *x, int *tot, int (*wsum)[4]) {
     }
 }
 
+// The plan's inputs staged in LDS when they fit (row_ptr, then the pair roles
+// and union lengths): both passes over the rows then read LDS instead of
+// waiting on global loads.
+constexpr int kPlanStage = 30 * 1024;     // int32 entries (120 KB)
+
 // Single workgroup.  Cost of a row = its kept key blocks.  chunk C: fixed,
 // none (INT_MAX) or automatic max(16, ceil(total / (8 * num_ctas))), which
 // keeps every item at most 1/8 of a workgroup's average share; a longer row
@@ -1258,8 +1268,37 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int R, int Nb, const
                                                             PlanHeader *hdr, WorkItem *items, SplitRow *splits) {
     __shared__ int tmp[kPlanThreads];
     __shared__ int head_at[kPlanThreads];   // emission position -> (b, h)
+    __shared__ int stage[kPlanStage];
     const int tid = threadIdx.x;
     const int BH = R / Nb;
+    {
+        const int n_role = role ? Nb : 0, n_ulen = role ? BH * max_pairs : 0;
+        const int n_all = R + 1 + n_role + n_ulen;
+        if ((int64_t)R + 1 + n_role + n_ulen <= kPlanStage) {
+            // eight loads in flight per thread and step
+            for (int x0 = 0; x0 < n_all; x0 += 8 * kPlanThreads) {
+                int val[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int x = x0 + u * kPlanThreads + tid;
+                    val[u] = (x <= R) ? row_ptr[x]
+                             : (x < R + 1 + n_role) ? role[x - R - 1]
+                             : (x < n_all) ? ulen[x - R - 1 - n_role] : 0;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int x = x0 + u * kPlanThreads + tid;
+                    if (x < n_all) stage[x] = val[u];
+                }
+            }
+            __syncthreads();
+            row_ptr = stage;
+            if (role) {
+                role = stage + R + 1;
+                ulen = stage + R + 1 + n_role;
+            }
+        }
+    }
     const bool by_density = BH <= kPlanThreads;
     if (by_density) {
         int mine = 0;
@@ -1276,9 +1315,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int R, int Nb, const
         __syncthreads();
     }
     // row emitted at position v
-    auto row_at = [&](int v) { return by_density ? head_at[v / Nb] * Nb + v % Nb : v; };
+    // This thread's rows: emission positions v = r0 .. r1 - 1, walked as
+    // (head slot hv = v / Nb, block i = v % Nb) without a division per row;
+    // the row at slot hv is that of head head_at[hv] (or hv itself).
     const int seg = (R + kPlanThreads - 1) / kPlanThreads;
     const int r0 = min(R, tid * seg), r1 = min(R, r0 + seg);
+    const int hv0 = r0 / Nb, i0 = r0 - hv0 * Nb;
     const int64_t total = row_ptr[R] - row_ptr[0];
     int C;
     if (chunk_mode < 0) C = INT32_MAX;
@@ -1287,11 +1329,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int R, int Nb, const
 
     // role of row r's query block under the current C: -1 alone, -2 second
     // of a pair, p >= 0 first of pair p
-    auto role_of = [&](int r) {
+    auto role_of = [&](int hb, int i) {
         if (!role) return -1;
-        const int i = r % Nb, rl = role[i];
+        const int rl = role[i];
         const int p = (rl >= 0) ? rl : (rl == -2 ? role[i - 1] : -1);
-        if (p < 0 || ulen[(r / Nb) * max_pairs + p] > C) return -1;
+        if (p < 0 || ulen[hb * max_pairs + p] > C) return -1;
         return rl;
     };
     __shared__ int wsum[kPlanThreads / 64][4];
@@ -1299,15 +1341,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int R, int Nb, const
     int cnt4[4], tot4[4];        // this thread's items, partial slots, split rows, pairs
     for (int attempt = 0; attempt < 2; ++attempt) {
         int li = 0, lp = 0, ls = 0, lq = 0;
-#pragma unroll 4
-        for (int v = r0; v < r1; ++v) {
-            const int r = row_at(v);
-            const int rl = role_of(r);
+        for (int v = r0, hv = hv0, i = i0; v < r1; ++v) {
+            const int hb = by_density ? head_at[hv] : hv;
+            const int r = hb * Nb + i;
+            const int rl = role_of(hb, i);
             const int n = (rl < 0) ? chunks_of(row_ptr[r + 1] - row_ptr[r], C) : 0;
             li += (rl >= 0) ? 1 : (rl == -1 ? n : 0);
             lq += (rl >= 0) ? 1 : 0;
             lp += (rl == -1 && n > 1) ? n : 0;
             ls += (rl == -1 && n > 1) ? 1 : 0;
+            if (++i == Nb) { i = 0; ++hv; }
         }
         cnt4[0] = li; cnt4[1] = lp; cnt4[2] = ls; cnt4[3] = lq;
         plan_scan4(cnt4, tot4, wsum);
@@ -1316,13 +1359,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int R, int Nb, const
         C = INT32_MAX;     // cannot happen for the automatic size; never overrun the workspace
     }
     int item = cnt4[0], part = cnt4[1], spl = cnt4[2];
-    for (int v = r0; v < r1; ++v) {
-        const int r = row_at(v);
-        const int rl = role_of(r);
+    for (int v = r0, hv = hv0, i = i0; v < r1; ++v) {
+        const int hb = by_density ? head_at[hv] : hv;
+        const int r = hb * Nb + i;
+        const int rl = role_of(hb, i);
+        const int i_row = i;
+        if (++i == Nb) { i = 0; ++hv; }
         if (rl == -2) continue;
         if (rl >= 0) {
-            const int slot = (r / Nb) * max_pairs + rl;
-            items[item++] = WorkItem{r, slot * Nb, slot * Nb + ulen[slot], -2 - (r % Nb + 1)};
+            const int slot = hb * max_pairs + rl;
+            items[item++] = WorkItem{r, slot * Nb, slot * Nb + ulen[slot], -2 - (i_row + 1)};
             continue;
         }
         const int b0 = row_ptr[r], cnt = row_ptr[r + 1] - b0;

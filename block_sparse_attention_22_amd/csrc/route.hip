@@ -557,25 +557,55 @@ __global__ __launch_bounds__(256) void head_total_kernel(Geo g, const int32_t *b
 constexpr int kAugThreads = 1024;
 constexpr int kAugRows = 2;            // rows per thread: Nb <= 2048
 
-// For the 15 thresholds t_v = x | (v << sh), v = 1..15: the first position
+// Augmentation resolves kAugBits bits of tau's bit pattern per round, with
+// one threshold per nonzero digit value.  Each threshold costs every row a
+// binary search on the one compute unit that serves the head, whose memory
+// pipeline is the limit: one bit per round (one search, more rounds) measured
+// fastest, ahead of 2, 3 and 4 bits (720p: 73, 76, 91 and 133 us).
+constexpr int kAugBits = 1;
+constexpr int kAugDigits = 1 << kAugBits;
+
+// For the thresholds t_v = x | (v << sh), v = 1 .. kAugDigits - 1: the first position
 // in [lo, hi) of a descending sorted row whose bit pattern is below t_v
 // (every position before it holds a value >= t_v), written to pos[v].  The
-// 15 binary searches run side by side for a common number of halvings, with
-// every probe issued unconditionally (index clamped to the row, result kept
-// only while the search is open), so one step waits for one round of loads
-// instead of 15 dependent chains.
-__device__ inline void first_below15(const double *row, int lo, int hi, int last, uint64_t x, int sh,
-                                     int *pos) {
-    int a[16], c[16];
+// bracket's first entry (its largest) and last entry (its smallest) settle
+// every threshold outside their range without a search; the rest run as
+// binary searches side by side, each halving one round of loads (only the
+// open searches load).
+__device__ inline void first_below_digits(const double *row, int lo, int hi, uint64_t x, int sh, int *pos) {
+    int a[kAugDigits], c[kAugDigits];
+    uint64_t top = 0, bot = 0;
+    if (lo < hi) {
+        top = double_bits(row[lo]);
+        bot = double_bits(row[hi - 1]);
+    }
 #pragma unroll
-    for (int v = 1; v < 16; ++v) { a[v] = lo; c[v] = hi; }
+    for (int v = 1; v < kAugDigits; ++v) {
+        const uint64_t t = x | ((uint64_t)v << sh);
+        if (lo >= hi || top < t) {
+            a[v] = c[v] = lo;            // no entry at or above t
+        } else if (bot >= t) {
+            a[v] = c[v] = hi;            // every entry at or above t
+        } else {
+            a[v] = lo + 1;               // row[lo] >= t > row[hi - 1]
+            c[v] = hi - 1;
+        }
+    }
     // each step leaves a bracket of n entries with at most floor(n / 2)
     for (int len = hi - lo; len > 0; len >>= 1) {
-        uint64_t bits[16];
+        bool any = false;
 #pragma unroll
-        for (int v = 1; v < 16; ++v) bits[v] = double_bits(row[min((a[v] + c[v]) >> 1, last)]);
+        for (int v = 1; v < kAugDigits; ++v) any |= a[v] < c[v];
+        if (!any) break;
+        uint64_t bits[kAugDigits];
 #pragma unroll
-        for (int v = 1; v < 16; ++v) {
+        for (int v = 1; v < kAugDigits; ++v) bits[v] = (a[v] < c[v]) ? double_bits(row[(a[v] + c[v]) >> 1]) : 0;
+        // Every open load leaves before the first compare waits: without
+        // this the scheduler interleaved them with the compares in groups,
+        // several dependent round trips per halving instead of one.
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int v = 1; v < kAugDigits; ++v) {
             const int mid = (a[v] + c[v]) >> 1;
             const bool open = a[v] < c[v];
             const bool above = bits[v] >= (x | ((uint64_t)v << sh));
@@ -584,26 +614,40 @@ __device__ inline void first_below15(const double *row, int lo, int hi, int last
         }
     }
 #pragma unroll
-    for (int v = 1; v < 16; ++v) pos[v] = a[v];
+    for (int v = 1; v < kAugDigits; ++v) pos[v] = a[v];
 }
 
-// First position in [lo, hi) of a descending sorted row whose bit pattern is
-// below t.
-__device__ inline int first_below(const double *row, int lo, int hi, uint64_t t) {
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (double_bits(row[mid]) >= t) lo = mid + 1;
-        else hi = mid;
+// First positions in [lo, hi) of a descending sorted row whose bit pattern
+// is below t0 and below t1: two binary searches side by side, so each
+// halving waits for one round of loads.
+__device__ inline void first_below2(const double *row, int lo, int hi, uint64_t t0, uint64_t t1, int *p0,
+                                    int *p1) {
+    int a0 = lo, c0 = hi, a1 = lo, c1 = hi;
+    const int last = max(lo, hi - 1);
+    for (int len = hi - lo; len > 0; len >>= 1) {
+        const int m0 = (a0 + c0) >> 1, m1 = (a1 + c1) >> 1;
+        const uint64_t b0 = double_bits(row[min(m0, last)]);
+        const uint64_t b1 = double_bits(row[min(m1, last)]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (a0 < c0) {
+            if (b0 >= t0) a0 = m0 + 1;
+            else c0 = m0;
+        }
+        if (a1 < c1) {
+            if (b1 >= t1) a1 = m1 + 1;
+            else c1 = m1;
+        }
     }
-    return lo;
+    *p0 = a0;
+    *p1 = a1;
 }
 
-constexpr int kAugGather = 1024;   // bracket size from which tau is picked directly
+constexpr int kAugGather = 512;    // bracket size from which tau is picked directly
 
 // One workgroup per (batch, head).  Chooses the A_h candidates (positions
 // r >= base_i of each row's sorted masses) with the largest mass, ties to
-// lower (i, j): a radix search over the IEEE bit pattern of the masses (four
-// bits per round, 15 thresholds at a time) narrows a per-row bracket around
+// lower (i, j): a radix search over the IEEE bit pattern of the masses
+// (kAugBits bits per round) narrows a per-row bracket around
 // the A_h-th largest mass tau; once the brackets hold at most kAugGather
 // entries together, tau is picked among them directly (rank counting in
 // LDS) and each row is re-bracketed to its entries equal to tau.  Rows take
@@ -612,7 +656,7 @@ constexpr int kAugGather = 1024;   // bracket size from which tau is picked dire
 __global__ __launch_bounds__(kAugThreads) void augment_kernel(Geo g, const double *SP, const int32_t *base,
                                                               int32_t *add, const int32_t *head_base,
                                                               int32_t *head_kept, int mode, double frac) {
-    __shared__ int cnt[16];
+    __shared__ int cnt[kAugDigits];
     __shared__ int tmp[kAugThreads];
     __shared__ int ired[kAugThreads / 64];
     __shared__ uint64_t gat[kAugGather];
@@ -651,9 +695,9 @@ __global__ __launch_bounds__(kAugThreads) void augment_kernel(Geo g, const doubl
     // Every candidate mass lies between the largest (the first entry of some
     // row's tail) and the smallest (the last entry of some row), so all of
     // them share the leading bits on which those two agree (bit patterns of
-    // masses >= 0 order like the masses).  The search starts at the 4-bit
-    // digit that holds their first difference, with x = the shared bits
-    // above it: the digits the rounds before it would have chosen.
+    // masses >= 0 order like the masses).  The search starts at the digit
+    // that holds their first difference, with x = the shared bits above it:
+    // the digits the rounds before it would have chosen.
     __shared__ uint64_t ured[kAugThreads / 64];
     uint64_t cmax = 0, cmin = ~0ull;
 #pragma unroll
@@ -667,22 +711,22 @@ __global__ __launch_bounds__(kAugThreads) void augment_kernel(Geo g, const doubl
     cmax = block_reduce<kAugThreads>(cmax, ured, [](uint64_t a, uint64_t c) { return max(a, c); });
     cmin = block_reduce<kAugThreads>(cmin, ured, [](uint64_t a, uint64_t c) { return min(a, c); });
     const uint64_t diff = cmax ^ cmin;
-    const int sh0 = diff ? ((63 - __clzll((long long)diff)) & ~3) : 0;
-    uint64_t x = (sh0 >= 60) ? 0 : (cmax >> (sh0 + 4)) << (sh0 + 4);
+    const int sh0 = diff ? ((63 - __clzll((long long)diff)) / kAugBits) * kAugBits : 0;
+    uint64_t x = (sh0 + kAugBits >= 64) ? 0 : (cmax >> (sh0 + kAugBits)) << (sh0 + kAugBits);
     bool direct = false;
-    for (int sh = sh0; sh >= 0; sh -= 4) {
-        if (tid < 16) cnt[tid] = 0;
+    for (int sh = sh0; sh >= 0; sh -= kAugBits) {
+        if (tid < kAugDigits) cnt[tid] = 0;
         __syncthreads();
-        int pos[kAugRows][16];
+        int pos[kAugRows][kAugDigits];
 #pragma unroll
         for (int q = 0; q < kAugRows; ++q) {
             pos[q][0] = hi[q];
             const double *row = SP + ((int64_t)bh * Nb + (q < nr ? r0 + q : 0)) * Nb;
             // rows past nr have lo = hi = 0: no step runs and every pos is 0
-            first_below15(row, lo[q], hi[q], Nb - 1, x, sh, pos[q]);
+            first_below_digits(row, lo[q], hi[q], x, sh, pos[q]);
         }
 #pragma unroll
-        for (int v = 1; v < 16; ++v) {
+        for (int v = 1; v < kAugDigits; ++v) {
             int c = 0;
 #pragma unroll
             for (int q = 0; q < kAugRows; ++q) c += (q < nr) ? pos[q][v] - m[q] : 0;
@@ -691,14 +735,14 @@ __global__ __launch_bounds__(kAugThreads) void augment_kernel(Geo g, const doubl
         }
         __syncthreads();
         int vs = 0;
-        for (int v = 15; v >= 1; --v)
+        for (int v = kAugDigits - 1; v >= 1; --v)
             if (cnt[v] >= A) { vs = v; break; }
         x |= (uint64_t)vs << sh;
 #pragma unroll
         for (int q = 0; q < kAugRows; ++q) {
             int nlo = lo[q], nhi = hi[q];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
+            for (int v = 0; v < kAugDigits; ++v) {
                 if (v == vs) nhi = pos[q][v];
                 if (v == vs + 1) nlo = pos[q][v];
             }
@@ -729,7 +773,15 @@ __global__ __launch_bounds__(kAugThreads) void augment_kernel(Geo g, const doubl
 #pragma unroll
         for (int q = 0; q < kAugRows; ++q) {
             const double *row = SP + ((int64_t)bh * Nb + (q < nr ? r0 + q : 0)) * Nb;
-            for (int pp = lo[q]; pp < hi[q]; ++pp) gat[o++] = double_bits(row[pp]);
+            // four loads in flight per step (the last one repeated past hi)
+            for (int pp = lo[q]; pp < hi[q]; pp += 4) {
+                uint64_t b[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) b[u] = double_bits(row[min(pp + u, hi[q] - 1)]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (pp + u < hi[q]) gat[o++] = b[u];
+            }
         }
         __syncthreads();
         // rank of entry e in (bits desc, e asc): unique, so one entry has rank_tau
@@ -748,9 +800,8 @@ __global__ __launch_bounds__(kAugThreads) void augment_kernel(Geo g, const doubl
         for (int q = 0; q < kAugRows; ++q) {
             if (q < nr) {
                 const double *row = SP + ((int64_t)bh * Nb + r0 + q) * Nb;
-                const int nlo = first_below(row, lo[q], hi[q], tau + 1);   // first entry <= tau
-                hi[q] = first_below(row, nlo, hi[q], tau);                   // first entry < tau
-                lo[q] = nlo;
+                // first entry <= tau, first entry < tau
+                first_below2(row, lo[q], hi[q], tau + 1, tau, &lo[q], &hi[q]);
             }
         }
     }
