@@ -126,12 +126,10 @@ __device__ inline int next_item_xcd(PlanHeader *hdr, int n_items, int &cur_q, in
             const int q = cur_q & 7;
             // items of queue q: (m * 8 + q) * kRun + w, w < kRun, below n_items
             const int cnt = rounds * kRun + min(kRun, max(0, rest - q * kRun));
-            if (__hip_atomic_load(&qs[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < cnt) {
-                const int t = atomicAdd(&qs[q], 1);
-                if (t < cnt) {
-                    it = ((t / kRun) * 8 + q) * kRun + t % kRun;
-                    break;
-                }
+            const int t = atomicAdd(&qs[q], 1);
+            if (t < cnt) {
+                it = ((t / kRun) * 8 + q) * kRun + t % kRun;
+                break;
             }
             ++cur_q;
         }
