@@ -138,7 +138,7 @@ fva_status static_scratch(void **ptr) {
 
 // ------------------------------------------------------ route workspace
 struct RouteWs {
-    size_t qbar, kbar, sp, order, base, add, head_base, head_kept, total;
+    size_t qbar, kbar, sp, order, base, add, head_kept, total;
 };
 
 RouteWs route_layout(const Geo &g) {
@@ -152,7 +152,6 @@ RouteWs route_layout(const Geo &g) {
     w.order = take(R * g.Nb * 4);
     w.base = take(R * 4);
     w.add = take(R * 4);
-    w.head_base = take((size_t)g.BH * 4);
     w.head_kept = take((size_t)g.BH * 4);
     w.total = off;
     return w;
@@ -346,7 +345,6 @@ fva_status route_launch(const Geo &g, const void *q, const void *k, double p, in
     char *W = static_cast<char *>(ws);
     double *qbar = (double *)(W + L.qbar), *kbar = (double *)(W + L.kbar), *SP = (double *)(W + L.sp);
     int32_t *order = (int32_t *)(W + L.order), *base = (int32_t *)(W + L.base), *add = (int32_t *)(W + L.add);
-    int32_t *head_base = (int32_t *)(W + L.head_base);
     int32_t *head_kept = out->head_kept ? out->head_kept : (int32_t *)(W + L.head_kept);
     if (!empty) {
         if (!pooled) {
@@ -355,7 +353,7 @@ fva_status route_launch(const Geo &g, const void *q, const void *k, double p, in
         }
         FVA_TRY_HIP(launch_scores(g, qbar, kbar, SP, s));
         FVA_TRY_HIP(launch_row_select(g, SP, order, base, p, kmin, s));
-        FVA_TRY_HIP(launch_augment(g, SP, base, add, head_base, head_kept, budget.mode, budget.frac, s));
+        FVA_TRY_HIP(launch_augment(g, SP, base, add, head_kept, budget.mode, budget.frac, s));
     }
     FVA_TRY_HIP(launch_csr(g, order, base, add, head_kept, out->row_ptr, out->col_idx, out->base_count, out->mask,
                            s));

@@ -9,11 +9,10 @@
 //   scores       s_ij = qbar_i . kbar_j / sqrt(d), float64 tiled GEMM
 //   row_select   one wave per query block: softmax, register bitonic sort by
 //                (mass desc, index asc), prefix sums, Top-p cut, Top-k floor
-//   head_total / augment
-//                per head: budget, then the not-yet-kept blocks with the
-//                largest mass (ties to lower (i, j)) found by a radix search
-//                over the sorted row tails
-//   scan / csr   row_ptr and ascending col_idx from a per-row bitmask
+//   augment      per head: base total and budget, then the not-yet-kept
+//                blocks with the largest mass (ties to lower (i, j)) found by
+//                a radix search over the sorted row tails
+//   csr          per row: its offset, and ascending col_idx from a bitmask
 // All routing arithmetic is float64 so the lists are deterministic and match
 // an independent float64 evaluation except at cumulative masses within
 // rounding of p.
@@ -545,15 +544,6 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) __attribute__((amdgpu_waves_per
 }
 
 // --------------------------------------------------------------- augment
-__global__ __launch_bounds__(256) void head_total_kernel(Geo g, const int32_t *base, int32_t *head_base) {
-    __shared__ int red[4];
-    const int bh = blockIdx.x;
-    int s = 0;
-    for (int i = threadIdx.x; i < g.Nb; i += 256) s += base[(int64_t)bh * g.Nb + i];
-    s = block_reduce<256>(s, red, [](int a, int b) { return a + b; });
-    if (threadIdx.x == 0) head_base[bh] = s;
-}
-
 constexpr int kAugThreads = 1024;
 constexpr int kAugRows = 2;            // rows per thread: Nb <= 2048
 
@@ -654,8 +644,8 @@ constexpr int kAugGather = 512;    // bracket size from which tau is picked dire
 // everything above tau, and the entries equal to tau go to the lowest rows
 // first (each row's equal entries are already in ascending j).
 __global__ __launch_bounds__(kAugThreads) void augment_kernel(Geo g, const double *SP, const int32_t *base,
-                                                              int32_t *add, const int32_t *head_base,
-                                                              int32_t *head_kept, int mode, double frac) {
+                                                              int32_t *add, int32_t *head_kept, int mode,
+                                                              double frac) {
     __shared__ int cnt[kAugDigits];
     __shared__ int tmp[kAugThreads];
     __shared__ int ired[kAugThreads / 64];
@@ -665,13 +655,26 @@ __global__ __launch_bounds__(kAugThreads) void augment_kernel(Geo g, const doubl
     const int b = bh / g.H;
     const int Nb = g.Nb;
     const int64_t NN = (int64_t)Nb * Nb;
-    const int K = head_base[bh];
+    // K = the head's kept blocks before augmentation (the sum of its rows'
+    // base counts); for match-max also the largest K among the heads of
+    // batch b, each wave summing whole heads.
+    int ks = 0;
+    for (int i = tid; i < Nb; i += kAugThreads) ks += base[(int64_t)bh * Nb + i];
+    const int K = block_reduce<kAugThreads>(ks, ired, [](int x, int y) { return x + y; });
     int64_t Bh = K;
     if (mode == FVA_BUDGET_FRAC) {
         Bh = K + (int64_t)floor(frac * (double)K);
         if (Bh > NN) Bh = NN;
     } else if (mode == FVA_BUDGET_MATCH_MAX) {
-        for (int hh = 0; hh < g.H; ++hh) Bh = max(Bh, (int64_t)head_base[b * g.H + hh]);
+        const int lane = tid & 63;
+        int kmax = 0;
+        for (int hh = tid >> 6; hh < g.H; hh += kAugThreads / 64) {
+            const int32_t *hb = base + (int64_t)(b * g.H + hh) * Nb;
+            int s = 0;
+            for (int i = lane; i < Nb; i += 64) s += hb[i];
+            kmax = max(kmax, wave_sum(s));
+        }
+        Bh = max(Bh, (int64_t)block_reduce<kAugThreads>(kmax, ired, [](int x, int y) { return max(x, y); }));
     }
     const int A = (int)(Bh - K);
     if (tid == 0) head_kept[bh] = (int)Bh;
@@ -826,48 +829,33 @@ __global__ __launch_bounds__(kAugThreads) void augment_kernel(Geo g, const doubl
 }
 
 // ------------------------------------------------------------ scan / csr
-constexpr int kScanThreads = 1024;
-
-// row_ptr[r] = sum of (base + add) over rows before r; row_ptr[R] = total.
-// One workgroup per (batch, head): its rows start after the kept blocks of
-// the heads before it (their totals B_h, which augmentation wrote), and are
-// scanned inside the workgroup.  Workgroup BH writes row_ptr[R].
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(Geo g, const int32_t *base, const int32_t *add,
-                                                            const int32_t *head_kept, int32_t *row_ptr,
-                                                            int32_t *base_out) {
-    __shared__ int tmp[kScanThreads];
-    __shared__ int red[kScanThreads / 64];
-    const int bh = blockIdx.x, tid = threadIdx.x, Nb = g.Nb;
-    int off = 0;
-    for (int h = tid; h < bh; h += kScanThreads) off += head_kept[h];
-    off = block_reduce<kScanThreads>(off, red, [](int a, int b) { return a + b; });
-    if (bh == g.BH) {
-        if (tid == 0) row_ptr[(int64_t)g.BH * Nb] = off;
-        return;
-    }
-    const int64_t r0 = (int64_t)bh * Nb;
-    const int seg = (Nb + kScanThreads - 1) / kScanThreads;
-    const int s0 = min(Nb, tid * seg), s1 = min(Nb, s0 + seg);
-    int local = 0;
-    for (int i = s0; i < s1; ++i) local += base[r0 + i] + add[r0 + i];
-    int total;
-    int run = off + block_exclusive_scan<kScanThreads>(local, tmp, &total);
-    for (int i = s0; i < s1; ++i) {
-        row_ptr[r0 + i] = run;
-        run += base[r0 + i] + add[r0 + i];
-        if (base_out) base_out[r0 + i] = base[r0 + i];
-    }
+// No rows: the CSR is row_ptr[0] = 0 (a kernel rather than a memset, so
+// that a captured graph replays it reliably).
+__global__ void empty_csr_kernel(int32_t *row_ptr) {
+    if (threadIdx.x == 0) row_ptr[0] = 0;
 }
 
-// One wave per row: bitmask of the first count entries of the row's order,
-// then set bits emitted in ascending order.
-__global__ __launch_bounds__(64) void csr_kernel(Geo g, const int32_t *order, const int32_t *row_ptr,
-                                                 int32_t *col_idx, uint32_t *mask) {
+// One wave per row: the row's offset (the kept blocks of the heads before
+// it, which augmentation wrote, plus those of the head's rows before it),
+// then a bitmask of the first count entries of the row's order, and the set
+// bits emitted in ascending order.  The last row also writes row_ptr[R].
+__global__ __launch_bounds__(64) void csr_kernel(Geo g, const int32_t *order, const int32_t *base,
+                                                 const int32_t *add, const int32_t *head_kept, int32_t *row_ptr,
+                                                 int32_t *col_idx, int32_t *base_out, uint32_t *mask) {
     __shared__ uint32_t bits[64];
     const int i = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
     const int Nk = g.Nb;
-    const int64_t row = (int64_t)bh * g.Nb + i;
-    const int start = row_ptr[row], cnt = row_ptr[row + 1] - start;
+    const int64_t row = (int64_t)bh * g.Nb + i, r0 = (int64_t)bh * g.Nb;
+    int before = 0;
+    for (int h = lane; h < bh; h += 64) before += head_kept[h];
+    for (int x = lane; x < i; x += 64) before += base[r0 + x] + add[r0 + x];
+    const int start = wave_sum(before);
+    const int cnt = base[row] + add[row];
+    if (lane == 0) {
+        row_ptr[row] = start;
+        if (row + 1 == (int64_t)g.BH * g.Nb) row_ptr[row + 1] = start + cnt;
+        if (base_out) base_out[row] = base[row];
+    }
     const int W = (Nk + 31) / 32;
     bits[lane] = 0;
     __syncthreads();
@@ -939,13 +927,10 @@ hipError_t launch_row_select(const Geo &g, double *SP, int32_t *order, int32_t *
     return hipGetLastError();
 }
 
-hipError_t launch_augment(const Geo &g, const double *SP, const int32_t *base, int32_t *add, int32_t *head_base,
-                          int32_t *head_kept, int mode, double frac, hipStream_t s) {
-    hipLaunchKernelGGL(head_total_kernel, dim3(g.BH), dim3(256), 0, s, g, base, head_base);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(augment_kernel, dim3(g.BH), dim3(kAugThreads), 0, s, g, SP, base, add, head_base,
-                       head_kept, mode, frac);
+hipError_t launch_augment(const Geo &g, const double *SP, const int32_t *base, int32_t *add, int32_t *head_kept,
+                          int mode, double frac, hipStream_t s) {
+    hipLaunchKernelGGL(augment_kernel, dim3(g.BH), dim3(kAugThreads), 0, s, g, SP, base, add, head_kept, mode,
+                       frac);
     return hipGetLastError();
 }
 
@@ -953,11 +938,13 @@ hipError_t launch_csr(const Geo &g, const int32_t *order, const int32_t *base, c
                       const int32_t *head_kept, int32_t *row_ptr, int32_t *col_idx, int32_t *base_out,
                       uint32_t *mask, hipStream_t s) {
     const int R = g.BH * g.Nb;
-    hipLaunchKernelGGL(scan_kernel, dim3(g.BH + 1), dim3(kScanThreads), 0, s, g, base, add, head_kept, row_ptr,
-                       base_out);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || R == 0) return e;
-    hipLaunchKernelGGL(csr_kernel, dim3(g.Nb, g.BH), dim3(64), 0, s, g, order, row_ptr, col_idx, mask);
+    if (R == 0) {
+        // no rows: only row_ptr[0] = 0
+        hipLaunchKernelGGL(empty_csr_kernel, dim3(1), dim3(64), 0, s, row_ptr);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(csr_kernel, dim3(g.Nb, g.BH), dim3(64), 0, s, g, order, base, add, head_kept, row_ptr,
+                       col_idx, base_out, mask);
     return hipGetLastError();
 }
 
