@@ -157,13 +157,16 @@ __global__ __launch_bounds__(256) void pool_kernel(Geo g, const T *x, double *ou
 // on the fp64 matrix cores: each wave owns a 32x32 quarter as 2x2 tiles of
 // v_mfma_f64_16x16x4f64 (A row i = lane%16, k = lane/16; B likewise; result
 // register r of a lane is row lane/16 + 4r, column lane%16), fed from LDS in
-// chunks of 32 along d.
+// chunks of 16 along d.  Small chunks (17 KB of LDS) and at most ~100
+// registers let five workgroups share a compute unit, which measured faster
+// (136 -> 113 us at 720p) than chunks of 32 at three workgroups.
 typedef __attribute__((ext_vector_type(4))) double f64x4;
 
-__global__ __launch_bounds__(256) void scores_kernel(Geo g, const double *qbar, const double *kbar,
-                                                     double *S) {
-    __shared__ double qs[64][33];
-    __shared__ double ks[64][33];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void scores_kernel(Geo g, const double *qbar,
+                                                                                             const double *kbar,
+                                                                                             double *S) {
+    __shared__ double qs[64][17];
+    __shared__ double ks[64][17];
     const int j0 = blockIdx.x * 64, i0 = blockIdx.y * 64, bh = blockIdx.z;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wy = w >> 1, wx = w & 1;
     const int l16 = lane & 15, kq = lane >> 4;
@@ -175,30 +178,30 @@ __global__ __launch_bounds__(256) void scores_kernel(Geo g, const double *qbar, 
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
-    // chunk d0 of both tiles: element e = threadIdx.x + 256 m is row e / 32,
-    // column e % 32; the next chunk is loaded into registers while the
+    // chunk d0 of both tiles: element e = threadIdx.x + 256 m is row e / 16,
+    // column e % 16; the next chunk is loaded into registers while the
     // current one is multiplied
-    double qr[8], kr[8];
+    double qr[4], kr[4];
     auto load_chunk = [&](int d0) {
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int e = threadIdx.x + 256 * m, r = e >> 5, cc = e & 31;
+        for (int m = 0; m < 4; ++m) {
+            const int e = threadIdx.x + 256 * m, r = e >> 4, cc = e & 15;
             qr[m] = (i0 + r < Nb) ? qb[(int64_t)(i0 + r) * g.D + d0 + cc] : 0.0;
             kr[m] = (j0 + r < Nb) ? kb[(int64_t)(j0 + r) * g.D + d0 + cc] : 0.0;
         }
     };
     load_chunk(0);
-    for (int d0 = 0; d0 < g.D; d0 += 32) {
+    for (int d0 = 0; d0 < g.D; d0 += 16) {
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int e = threadIdx.x + 256 * m, r = e >> 5, cc = e & 31;
+        for (int m = 0; m < 4; ++m) {
+            const int e = threadIdx.x + 256 * m, r = e >> 4, cc = e & 15;
             qs[r][cc] = qr[m];
             ks[r][cc] = kr[m];
         }
         __syncthreads();
-        if (d0 + 32 < g.D) load_chunk(d0 + 32);
+        if (d0 + 16 < g.D) load_chunk(d0 + 16);
 #pragma unroll
-        for (int kk = 0; kk < 32; kk += 4) {
+        for (int kk = 0; kk < 16; kk += 4) {
             double av[2], bv[2];
 #pragma unroll
             for (int a = 0; a < 2; ++a) av[a] = qs[32 * wy + 16 * a + l16][kk + kq];
@@ -418,10 +421,11 @@ __device__ __forceinline__ void bitonic_keys(uint64_t *key, int lane, int e0) {
 
 constexpr int kIdxMask = 2047;     // index field of the sort key: rows of up to 2,048 slots
 
-// The first launch asks for three waves per SIMD: at 32 slots per lane that
-// costs a few spilled registers and measured faster than two waves.
+// The first launch asks for five waves per SIMD at up to 16 slots per lane
+// and three at 32: each costs a few spilled registers and measured faster
+// than fewer waves.
 template <int E, bool EXACT>
-__global__ __launch_bounds__(64 * kRowsPerGroup) __attribute__((amdgpu_waves_per_eu(EXACT ? 1 : 3))) void row_select_kernel(Geo g, double *SP, int32_t *order,
+__global__ __launch_bounds__(64 * kRowsPerGroup) __attribute__((amdgpu_waves_per_eu(EXACT ? 1 : (E >= 32 ? 3 : 5)))) void row_select_kernel(Geo g, double *SP, int32_t *order,
                                                                         int32_t *base, double p, int kmin) {
     static_assert(64 * E <= kIdxMask + 1, "slot indices must fit the key's index field");
     const int lane = threadIdx.x & 63;
