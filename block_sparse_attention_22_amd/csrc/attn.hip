@@ -1476,19 +1476,26 @@ __device__ inline void store4<uint16_t>(uint16_t *p, float4 v) {
     *reinterpret_cast<uint2 *>(p) = make_uint2(a, b);
 }
 
+// Workgroups per split row, each merging 16 of its query slots: the merge of
+// one element is a short chain of dependent loads, so a row spread over
+// eight workgroups finishes in two such chains per thread instead of 16.
+constexpr int kCombineSlices = 8;
+
 template <typename OutT>
 __global__ __launch_bounds__(256) void combine_kernel(Geo g, OutT *O, const int32_t *tok, const int32_t *bsize,
                                                       const PlanHeader *hdr, const SplitRow *splits,
                                                       const float *part_o, const float *part_ml) {
     const int n_split = hdr->info.n_split_rows;
     const int D4 = g.D / 4;
-    for (int sidx = blockIdx.x; sidx < n_split; sidx += gridDim.x) {
+    constexpr int kSlotsPerSlice = kMaxSlots / kCombineSlices;
+    for (int wi = blockIdx.x; wi < n_split * kCombineSlices; wi += gridDim.x) {
+        const int sidx = wi / kCombineSlices, q0 = (wi % kCombineSlices) * kSlotsPerSlice;
         const SplitRow sr = splits[sidx];
         const int bh = sr.row / g.Nb, i = sr.row - (sr.row / g.Nb) * g.Nb;
         const int64_t boff = (int64_t)(bh / g.H) * g.sb + (int64_t)(bh % g.H) * g.sh;
-        const int n_i = bsize[i];
-        for (int e = threadIdx.x; e < n_i * D4; e += 256) {
-            const int q = e / D4, c4 = e - (e / D4) * D4;
+        const int nq = min(bsize[i] - q0, kSlotsPerSlice);
+        for (int e = threadIdx.x; e < nq * D4; e += 256) {
+            const int q = q0 + e / D4, c4 = e - (e / D4) * D4;
             float M = -INFINITY;
             for (int p = 0; p < sr.n_parts; ++p)
                 M = fmaxf(M, part_ml[((int64_t)(sr.part_begin + p) * kMaxSlots + q) * 2]);
@@ -1604,7 +1611,8 @@ hipError_t launch_combine(const Geo &g, void *o, const int32_t *tok, const int32
                           const SplitRow *splits, const float *part_o, const float *part_ml, int cap_splits,
                           hipStream_t s) {
     if (cap_splits <= 0) return hipSuccess;
-    const int grid = cap_splits < 1024 ? cap_splits : 1024;
+    const int64_t want = (int64_t)cap_splits * kCombineSlices;
+    const int grid = want < 2048 ? (int)want : 2048;
     if (g.dtype == FVA_BF16)
         hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(grid), dim3(256), 0, s, g, (uint16_t *)o, tok, bsize, hdr,
                            splits, part_o, part_ml);
