@@ -877,17 +877,22 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
 // Block-major copies for the d=128 kernel, one workgroup per (block,
 // batch*head): Kp[(bh*Nb + j)*128 + slot][128] and, per 8-slot group g,
 // Vg[((bh*Nb + j)*16 + g)*128 + dd][8 slots] (V^T of the group, 2 KB
-// contiguous), slots past the block's tokens zero.  Every global access is
+// contiguous); the slots of a block's last group past its tokens are zero,
+// and groups wholly past its tokens are never written.  Every global access is
 // a 256-byte row moved by 16 lanes (K, V reads; K writes) or 16-byte
 // chunks consecutive across lanes (V^T writes): V goes through LDS, where
 // thread t builds chunks t, t + 256, ... of the block's V^T from eight
 // 2-byte reads of one column each (the 64 lanes of a wave read 64
 // consecutive columns of one row: no bank conflicts).
+// Slots past the block's tokens are not loaded (zero).
 __device__ __forceinline__ void load_rows(u32x4 *x, const uint16_t *T, const BlockTokens &bt, int64_t hoff,
                                           int64_t sn, int c16, int hi) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
-        x[m] = *reinterpret_cast<const u32x4 *>(T + hoff + (int64_t)bt.token(hi + 16 * m) * sn + c16 * 8);
+    for (int m = 0; m < 8; ++m) {
+        x[m] = u32x4{0, 0, 0, 0};
+        if (hi + 16 * m < bt.n)
+            x[m] = *reinterpret_cast<const u32x4 *>(T + hoff + (int64_t)bt.token(hi + 16 * m) * sn + c16 * 8);
+    }
 }
 
 __device__ __forceinline__ void stage_rows(uint16_t *vs, const u32x4 *x, int c16, int hi) {
@@ -895,21 +900,26 @@ __device__ __forceinline__ void stage_rows(uint16_t *vs, const u32x4 *x, int c16
     for (int m = 0; m < 8; ++m) *reinterpret_cast<u32x4 *>(vs + (hi + 16 * m) * 128 + c16 * 8) = x[m];
 }
 
-__device__ __forceinline__ void write_k_rows(uint16_t *Kp_blk, u32x4 *x, int n, int c16, int hi) {
+// Rows of the block's tokens, and zero rows up to the next multiple of 8:
+// the attention reads whole 8-slot groups of a block's tokens and nothing
+// past them, so later groups are left unwritten.
+__device__ __forceinline__ void write_k_rows(uint16_t *Kp_blk, const u32x4 *x, int n, int c16, int hi) {
+    const int n8 = (n + 7) & ~7;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
         const int slot = hi + 16 * m;
-        if (slot >= n) x[m] = u32x4{0, 0, 0, 0};
-        *reinterpret_cast<u32x4 *>(Kp_blk + slot * 128 + c16 * 8) = x[m];
+        if (slot < n8) *reinterpret_cast<u32x4 *>(Kp_blk + slot * 128 + c16 * 8) = x[m];
     }
 }
 
-// After a barrier behind stage_rows: the block's V^T chunks from LDS.
+// After a barrier behind stage_rows: the block's V^T chunks from LDS, for
+// the 8-slot groups that hold tokens (slots past the tokens zero).
 __device__ __forceinline__ void write_vt_groups(uint16_t *Vt_blk, const uint16_t *vs, int n) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int c = threadIdx.x + 256 * i;          // chunk (g, dd) = (c / 128, c % 128)
         const int r0 = 8 * (c >> 7), dd = c & 127;
+        if (r0 >= n) continue;
         u32x4 o;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {

@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void s
         }
         __syncthreads();
     }
-    const double sq = sqrt((double)g.D);
+    const double rsq = 1.0 / sqrt((double)g.D);
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void s
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = i0 + 32 * wy + 16 * a + kq + 4 * r;
-                if (i < Nb && j < Nb) S[((int64_t)bh * Nb + i) * Nb + j] = acc[a][b][r] / sq;
+                if (i < Nb && j < Nb) S[((int64_t)bh * Nb + i) * Nb + j] = acc[a][b][r] * rsq;
             }
         }
 }
@@ -436,15 +436,19 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) __attribute__((amdgpu_waves_per
     double *srow = SP + row * Nk;
     const int e0 = lane * E;
 
+    // Before the sort, entry r of a lane holds slot r * 64 + lane, so each
+    // load is 64 consecutive scores; the network orders by (mass, slot), so
+    // where an entry starts does not matter.  After the sort, entry r of a
+    // lane is sorted position e0 + r.
     double v[E];
     int id[E];
     double mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < E; ++r) {
-        const bool in = e0 + r < Nk;
-        const double x = srow[min(e0 + r, Nk - 1)];
-        v[r] = in ? x : -INFINITY;
-        id[r] = e0 + r;
+        const int sl = r * 64 + lane;
+        const double x = srow[min(sl, Nk - 1)];
+        v[r] = (sl < Nk) ? x : -INFINITY;
+        id[r] = sl;
         mx = fmax(mx, v[r]);
     }
     mx = wave_max(mx);
@@ -465,16 +469,18 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) __attribute__((amdgpu_waves_per
         // key would break the network's permutation).  Wave-uniform.
 #pragma unroll
         for (int r = 0; r < E; ++r) {
-            if (e0 + r < Nk) {
-                srow[e0 + r] = 0.0;
-                orow[e0 + r] = e0 + r;
+            const int sl = r * 64 + lane;
+            if (sl < Nk) {
+                srow[sl] = 0.0;
+                orow[sl] = sl;
             }
         }
         if (lane == 0) base[row] = Nk;
         return;
     }
+    const double inv = 1.0 / sum;
 #pragma unroll
-    for (int r = 0; r < E; ++r) v[r] = (e0 + r < Nk) ? v[r] / sum : 0.0;   // padding: +0, index >= Nk
+    for (int r = 0; r < E; ++r) v[r] = (id[r] < Nk) ? v[r] * inv : 0.0;   // padding: +0, index >= Nk
 
     if (EXACT) {
         bitonic_row<E>(v, id, lane, e0);
@@ -493,8 +499,8 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) __attribute__((amdgpu_waves_per
 #pragma unroll
         for (int r = 0; r < E; ++r) {
             const uint64_t bits = (uint64_t)__double_as_longlong(v[r]);
-            prow[e0 + r] = (uint16_t)(bits & kIdxMask);
-            key[r] = (bits & ~(uint64_t)kIdxMask) | (uint32_t)(kIdxMask - (e0 + r));
+            prow[id[r]] = (uint16_t)(bits & kIdxMask);
+            key[r] = (bits & ~(uint64_t)kIdxMask) | (uint32_t)(kIdxMask - id[r]);
         }
         bitonic_keys<E>(key, lane, e0);
 #pragma unroll
