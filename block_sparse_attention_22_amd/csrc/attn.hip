@@ -884,15 +884,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d128_kernel(AttnArgs a, cons
 // thread t builds chunks t, t + 256, ... of the block's V^T from eight
 // 2-byte reads of one column each (the 64 lanes of a wave read 64
 // consecutive columns of one row: no bank conflicts).
-// Slots past the block's tokens are not loaded (zero).
+// Slots past the block's tokens re-read its first token (loads stay
+// unconditional, so they are all in flight at once); every consumer masks
+// them by the block's token count.
 __device__ __forceinline__ void load_rows(u32x4 *x, const uint16_t *T, const BlockTokens &bt, int64_t hoff,
                                           int64_t sn, int c16, int hi) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        x[m] = u32x4{0, 0, 0, 0};
-        if (hi + 16 * m < bt.n)
-            x[m] = *reinterpret_cast<const u32x4 *>(T + hoff + (int64_t)bt.token(hi + 16 * m) * sn + c16 * 8);
-    }
+    for (int m = 0; m < 8; ++m)
+        x[m] = *reinterpret_cast<const u32x4 *>(T + hoff + (int64_t)bt.token(hi + 16 * m) * sn + c16 * 8);
 }
 
 __device__ __forceinline__ void stage_rows(uint16_t *vs, const u32x4 *x, int c16, int hi) {
@@ -903,11 +902,12 @@ __device__ __forceinline__ void stage_rows(uint16_t *vs, const u32x4 *x, int c16
 // Rows of the block's tokens, and zero rows up to the next multiple of 8:
 // the attention reads whole 8-slot groups of a block's tokens and nothing
 // past them, so later groups are left unwritten.
-__device__ __forceinline__ void write_k_rows(uint16_t *Kp_blk, const u32x4 *x, int n, int c16, int hi) {
+__device__ __forceinline__ void write_k_rows(uint16_t *Kp_blk, u32x4 *x, int n, int c16, int hi) {
     const int n8 = (n + 7) & ~7;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
         const int slot = hi + 16 * m;
+        if (slot >= n) x[m] = u32x4{0, 0, 0, 0};
         if (slot < n8) *reinterpret_cast<u32x4 *>(Kp_blk + slot * 128 + c16 * 8) = x[m];
     }
 }
