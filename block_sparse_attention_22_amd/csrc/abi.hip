@@ -219,7 +219,7 @@ fva_status attn_sizes(const Geo &g, const fva_attn_options *opts, AttnPlanSizes 
 
 struct AttnWs {
     size_t tok, bsize, hdr, items, splits, part_o, part_ml, kp, vt;
-    size_t role, first, n_pairs, ucol, ulen, total;
+    size_t role, first, n_pairs, ucol, ulen, hc, total;
 };
 
 AttnWs attn_layout(const Geo &g, const AttnPlanSizes &s) {
@@ -240,6 +240,7 @@ AttnWs attn_layout(const Geo &g, const AttnPlanSizes &s) {
     w.n_pairs = take(4);
     w.ucol = take((size_t)g.BH * s.max_pairs * g.Nb * 4);
     w.ulen = take((size_t)g.BH * s.max_pairs * 4);
+    w.hc = take((size_t)g.BH * 8 * 4);           // the plan's per-head counts
     w.total = off;
     return w;
 }
@@ -429,7 +430,7 @@ fva_status attn_launch(const Geo &g, const AttnPlanSizes &sz, const void *q, con
     FVA_TRY_HIP(launch_slot_table(g, tok, bsize, s));
     FVA_TRY_HIP(launch_row_pairs(g, bsize, lists->row_ptr, lists->col_idx, rp, s));
     FVA_TRY_HIP(launch_plan(g, lists->row_ptr, chunk, sz.num_ctas, sz.cap_items, sz.cap_parts, rp, hdr, items, splits,
-                            s));
+                            (int32_t *)(W + L.hc), s));
     if (stats) FVA_TRY_HIP(launch_plan_stats(g, lists->row_ptr, lists->col_idx, bsize, sz.num_ctas, items, hdr, s));
     hipEvent_t ev0 = opts ? (hipEvent_t)opts->kernel_events[0] : nullptr;
     hipEvent_t ev1 = opts ? (hipEvent_t)opts->kernel_events[1] : nullptr;

@@ -1216,14 +1216,44 @@ __global__ __launch_bounds__(64) void pair_union_kernel(int Nb, int max_pairs, c
 }
 
 // ------------------------------------------------------------------ plan
-constexpr int kPlanThreads = 1024;
+// The plan, one workgroup per (batch, head) in two launches.  Cost of a row =
+// its kept key blocks.  Chunk C: fixed, none (INT_MAX) or automatic
+// max(16, ceil(total / (8 * num_ctas))), which keeps every item at most 1/8 of
+// a workgroup's average share; a longer row is cut into ceil(cnt / C)
+// near-equal chunks, each a work item with its own partial slot.  Heads are
+// emitted densest first (by kept blocks, ties to the lower (b, h); in (b, h)
+// order when there are more than kPlanOrderMax heads), rows of a head in
+// order: the long items of dense heads start early and the short items of
+// sparse heads fill the end of the queues, and concurrently running
+// workgroups read the same head's keys and values.  With row pairs (role !=
+// null), a pair whose union list holds at most C blocks is one item over that
+// list, emitted at the place of its first block and never split; a longer
+// pair runs as two rows, so that they can still be split.  If the items or
+// partial slots of C overrun the workspace, C becomes INT_MAX (cannot happen
+// for the automatic size).
+//   plan_count_kernel: each head's items, partial slots, split rows and pairs,
+//     for C and for INT_MAX (eight counts per head);
+//   plan_emit_kernel: each head settles C from all heads' counts, finds its
+//     place in the emission order and the counts of the heads before it, and
+//     writes its rows' items (a workgroup scan gives each thread's offsets).
+constexpr int kPlanThreads = 256;
+constexpr int kPlanOrderMax = 1024;        // heads ordered by density up to this many
+constexpr int kPlanMaxRows = 2048;         // query blocks per head
+constexpr int kPlanMaxPairs = 1024;
 
 __device__ inline int chunks_of(int cnt, int C) { return (cnt > C) ? (cnt + C - 1) / C : 1; }
 
+__device__ inline int plan_chunk(int chunk_mode, int64_t total, int num_ctas) {
+    if (chunk_mode < 0) return INT32_MAX;
+    if (chunk_mode > 0) return chunk_mode;
+    return (int)max((int64_t)16, (total + 8LL * num_ctas - 1) / (8LL * num_ctas));
+}
+
 // Exclusive scan of four per-thread counts over the workgroup (wave scans by
-// lane shuffles, then the 16 wave totals through LDS): x becomes the sum over
-// the threads before this one, tot the sum over all.
+// lane shuffles, then the wave totals through LDS): x becomes the sum over the
+// threads before this one, tot the sum over all.
 __device__ inline void plan_scan4(int *x, int *tot, int (*wsum)[4]) {
+    constexpr int NW = kPlanThreads / 64;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     int incl[4];
 #pragma unroll
@@ -1243,7 +1273,8 @@ __device__ inline void plan_scan4(int *x, int *tot, int (*wsum)[4]) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         int before = 0, all = 0;
-        for (int i = 0; i < kPlanThreads / 64; ++i) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
             const int v = wsum[i][c];
             before += (i < w) ? v : 0;
             all += v;
@@ -1253,153 +1284,151 @@ __device__ inline void plan_scan4(int *x, int *tot, int (*wsum)[4]) {
     }
 }
 
-// The plan's inputs staged in LDS when they fit (row_ptr, then the pair roles
-// and union lengths): both passes over the rows then read LDS instead of
-// waiting on global loads.
-constexpr int kPlanStage = 30 * 1024;     // int32 entries (120 KB)
+// One head's plan inputs in LDS: its Nb + 1 row_ptr entries, the pair roles
+// and its union lengths.
+struct PlanHead {
+    int rp[kPlanMaxRows + 1];
+    int role[kPlanMaxRows];
+    int ulen[kPlanMaxPairs];
+};
 
-// Single workgroup.  Cost of a row = its kept key blocks.  chunk C: fixed,
-// none (INT_MAX) or automatic max(16, ceil(total / (8 * num_ctas))), which
-// keeps every item at most 1/8 of a workgroup's average share; a longer row
-// is cut into ceil(cnt / C) near-equal chunks, each a work item with its own
-// partial slot.  Heads are emitted densest first (by kept blocks, ties to the
-// lower (b, h); in (b, h) order when there are more than kPlanThreads heads),
-// rows of a head in order: the long items of dense heads start early and the
-// short items of sparse heads fill the end of the queues, and concurrently
-// running workgroups read the same head's keys and values.  With row pairs
-// (role != null), a pair whose union list holds at most C blocks is one item
-// over that list, emitted at the place of its first block and never split;
-// a longer pair runs as two rows, so that they can still be split.
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(int R, int Nb, const int32_t *row_ptr, int chunk_mode,
-                                                            int num_ctas, int cap_items, int cap_parts,
-                                                            const int32_t *role, const int32_t *ulen, int max_pairs,
-                                                            PlanHeader *hdr, WorkItem *items, SplitRow *splits) {
-    __shared__ int tmp[kPlanThreads];
-    __shared__ int head_at[kPlanThreads];   // emission position -> (b, h)
-    __shared__ int stage[kPlanStage];
-    const int tid = threadIdx.x;
-    const int BH = R / Nb;
-    {
-        const int n_role = role ? Nb : 0, n_ulen = role ? BH * max_pairs : 0;
-        const int n_all = R + 1 + n_role + n_ulen;
-        if ((int64_t)R + 1 + n_role + n_ulen <= kPlanStage) {
-            // eight loads in flight per thread and step
-            for (int x0 = 0; x0 < n_all; x0 += 8 * kPlanThreads) {
-                int val[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int x = x0 + u * kPlanThreads + tid;
-                    val[u] = (x <= R) ? row_ptr[x]
-                             : (x < R + 1 + n_role) ? role[x - R - 1]
-                             : (x < n_all) ? ulen[x - R - 1 - n_role] : 0;
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int x = x0 + u * kPlanThreads + tid;
-                    if (x < n_all) stage[x] = val[u];
-                }
-            }
-            __syncthreads();
-            row_ptr = stage;
-            if (role) {
-                role = stage + R + 1;
-                ulen = stage + R + 1 + n_role;
-            }
-        }
+__device__ inline void stage_head(PlanHead &ph, int hb, int Nb, const int32_t *row_ptr, const int32_t *role,
+                                  const int32_t *ulen, int max_pairs) {
+    for (int x = threadIdx.x; x <= Nb; x += kPlanThreads) ph.rp[x] = row_ptr[(int64_t)hb * Nb + x];
+    if (role) {
+        for (int x = threadIdx.x; x < Nb; x += kPlanThreads) ph.role[x] = role[x];
+        for (int x = threadIdx.x; x < max_pairs; x += kPlanThreads) ph.ulen[x] = ulen[(int64_t)hb * max_pairs + x];
     }
-    const bool by_density = BH <= kPlanThreads;
-    if (by_density) {
-        int mine = 0;
-        if (tid < BH) {
-            mine = row_ptr[(tid + 1) * Nb] - row_ptr[tid * Nb];
-            tmp[tid] = mine;
-        }
-        __syncthreads();
-        if (tid < BH) {
-            int rank = 0;
-            for (int h2 = 0; h2 < BH; ++h2) rank += (tmp[h2] > mine || (tmp[h2] == mine && h2 < tid)) ? 1 : 0;
-            head_at[rank] = tid;
-        }
-        __syncthreads();
-    }
-    // row emitted at position v
-    // This thread's rows: emission positions v = r0 .. r1 - 1, walked as
-    // (head slot hv = v / Nb, block i = v % Nb) without a division per row;
-    // the row at slot hv is that of head head_at[hv] (or hv itself).
-    const int seg = (R + kPlanThreads - 1) / kPlanThreads;
-    const int r0 = min(R, tid * seg), r1 = min(R, r0 + seg);
-    const int hv0 = r0 / Nb, i0 = r0 - hv0 * Nb;
-    const int64_t total = row_ptr[R] - row_ptr[0];
-    int C;
-    if (chunk_mode < 0) C = INT32_MAX;
-    else if (chunk_mode > 0) C = chunk_mode;
-    else C = (int)max((int64_t)16, (total + 8LL * num_ctas - 1) / (8LL * num_ctas));
+    __syncthreads();
+}
 
-    // role of row r's query block under the current C: -1 alone, -2 second
-    // of a pair, p >= 0 first of pair p
-    auto role_of = [&](int hb, int i) {
-        if (!role) return -1;
-        const int rl = role[i];
-        const int p = (rl >= 0) ? rl : (rl == -2 ? role[i - 1] : -1);
-        if (p < 0 || ulen[hb * max_pairs + p] > C) return -1;
-        return rl;
-    };
+// Role of query block i under chunk C: -1 alone, -2 second of a pair, p >= 0
+// first of pair p.
+__device__ inline int plan_role(const PlanHead &ph, bool pairs, int i, int C) {
+    if (!pairs) return -1;
+    const int rl = ph.role[i];
+    const int p = (rl >= 0) ? rl : (rl == -2 ? ph.role[i - 1] : -1);
+    if (p < 0 || ph.ulen[p] > C) return -1;
+    return rl;
+}
+
+// This thread's rows [i0, i1) of the head: items, partial slots, split rows, pairs.
+__device__ inline void plan_count_rows(const PlanHead &ph, bool pairs, int i0, int i1, int C, int *c4) {
+    int li = 0, lp = 0, ls = 0, lq = 0;
+    for (int i = i0; i < i1; ++i) {
+        const int rl = plan_role(ph, pairs, i, C);
+        const int n = (rl < 0) ? chunks_of(ph.rp[i + 1] - ph.rp[i], C) : 0;
+        li += (rl >= 0) ? 1 : (rl == -1 ? n : 0);
+        lq += (rl >= 0) ? 1 : 0;
+        lp += (rl == -1 && n > 1) ? n : 0;
+        ls += (rl == -1 && n > 1) ? 1 : 0;
+    }
+    c4[0] = li; c4[1] = lp; c4[2] = ls; c4[3] = lq;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(int BH, int Nb, const int32_t *row_ptr,
+                                                                  int chunk_mode, int num_ctas, const int32_t *role,
+                                                                  const int32_t *ulen, int max_pairs, int32_t *hc) {
+    __shared__ PlanHead ph;
     __shared__ int wsum[kPlanThreads / 64][4];
-    int n_items = 0, n_parts = 0, n_splits = 0, n_pairs = 0;
-    int cnt4[4], tot4[4];        // this thread's items, partial slots, split rows, pairs
-    for (int attempt = 0; attempt < 2; ++attempt) {
-        int li = 0, lp = 0, ls = 0, lq = 0;
-        for (int v = r0, hv = hv0, i = i0; v < r1; ++v) {
-            const int hb = by_density ? head_at[hv] : hv;
-            const int r = hb * Nb + i;
-            const int rl = role_of(hb, i);
-            const int n = (rl < 0) ? chunks_of(row_ptr[r + 1] - row_ptr[r], C) : 0;
-            li += (rl >= 0) ? 1 : (rl == -1 ? n : 0);
-            lq += (rl >= 0) ? 1 : 0;
-            lp += (rl == -1 && n > 1) ? n : 0;
-            ls += (rl == -1 && n > 1) ? 1 : 0;
-            if (++i == Nb) { i = 0; ++hv; }
-        }
-        cnt4[0] = li; cnt4[1] = lp; cnt4[2] = ls; cnt4[3] = lq;
-        plan_scan4(cnt4, tot4, wsum);
-        n_items = tot4[0]; n_parts = tot4[1]; n_splits = tot4[2]; n_pairs = tot4[3];
-        if (n_items <= cap_items && n_parts <= cap_parts) break;
-        C = INT32_MAX;     // cannot happen for the automatic size; never overrun the workspace
+    const int hb = blockIdx.x;
+    stage_head(ph, hb, Nb, row_ptr, role, ulen, max_pairs);
+    const int C = plan_chunk(chunk_mode, (int64_t)row_ptr[(int64_t)BH * Nb] - row_ptr[0], num_ctas);
+    const int seg = (Nb + kPlanThreads - 1) / kPlanThreads;
+    const int i0 = min(Nb, (int)threadIdx.x * seg), i1 = min(Nb, i0 + seg);
+    int c4[4], tot[4];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        plan_count_rows(ph, role != nullptr, i0, i1, k ? INT32_MAX : C, c4);
+        plan_scan4(c4, tot, wsum);
+        if (threadIdx.x == 0)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) hc[(int64_t)hb * 8 + 4 * k + c] = tot[c];
     }
-    int item = cnt4[0], part = cnt4[1], spl = cnt4[2];
-    for (int v = r0, hv = hv0, i = i0; v < r1; ++v) {
-        const int hb = by_density ? head_at[hv] : hv;
-        const int r = hb * Nb + i;
-        const int rl = role_of(hb, i);
-        const int i_row = i;
-        if (++i == Nb) { i = 0; ++hv; }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_emit_kernel(int BH, int Nb, const int32_t *row_ptr,
+                                                                 int chunk_mode, int num_ctas, int cap_items,
+                                                                 int cap_parts, const int32_t *role,
+                                                                 const int32_t *ulen, int max_pairs,
+                                                                 const int32_t *hc, PlanHeader *hdr, WorkItem *items,
+                                                                 SplitRow *splits) {
+    __shared__ PlanHead ph;
+    __shared__ int wsum[kPlanThreads / 64][4];
+    const int hb = blockIdx.x, tid = threadIdx.x;
+    const int64_t total = (int64_t)row_ptr[(int64_t)BH * Nb] - row_ptr[0];
+    // C for all heads, then the heads emitted before this one (their items,
+    // partial slots and split rows) and the totals.
+    int a4[4] = {0, 0, 0, 0};
+    for (int h2 = tid; h2 < BH; h2 += kPlanThreads) {
+        a4[0] += hc[(int64_t)h2 * 8 + 0];
+        a4[1] += hc[(int64_t)h2 * 8 + 1];
+    }
+    int t4[4];
+    plan_scan4(a4, t4, wsum);
+    const int C0 = plan_chunk(chunk_mode, total, num_ctas);
+    const bool wide = t4[0] > cap_items || t4[1] > cap_parts;     // never overrun the workspace
+    const int C = wide ? INT32_MAX : C0;
+    const int k = wide ? 4 : 0;
+    const bool by_density = BH <= kPlanOrderMax;
+    const int mine = row_ptr[(int64_t)(hb + 1) * Nb] - row_ptr[(int64_t)hb * Nb];
+    int b4[4] = {0, 0, 0, 0}, all4[4] = {0, 0, 0, 0};
+    for (int h2 = tid; h2 < BH; h2 += kPlanThreads) {
+        bool before = h2 < hb;
+        if (by_density) {
+            const int t2 = row_ptr[(int64_t)(h2 + 1) * Nb] - row_ptr[(int64_t)h2 * Nb];
+            before = t2 > mine || (t2 == mine && h2 < hb);
+        }
+        const int32_t *c = hc + (int64_t)h2 * 8 + k;
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            b4[q] += before ? c[q] : 0;
+            all4[q] += c[q];
+        }
+        all4[3] += c[3];
+    }
+    int s4[4], n4[4];
+    plan_scan4(b4, s4, wsum);          // s4: the heads emitted before this one
+    plan_scan4(all4, n4, wsum);        // n4: all heads (items, partial slots, split rows, pairs)
+    stage_head(ph, hb, Nb, row_ptr, role, ulen, max_pairs);
+    const bool pairs = role != nullptr;
+    const int seg = (Nb + kPlanThreads - 1) / kPlanThreads;
+    const int i0 = min(Nb, tid * seg), i1 = min(Nb, i0 + seg);
+    int c4[4], tot[4];
+    plan_count_rows(ph, pairs, i0, i1, C, c4);
+    plan_scan4(c4, tot, wsum);
+    int item = s4[0] + c4[0], part = s4[1] + c4[1], spl = s4[2] + c4[2];
+    const int r0 = hb * Nb;
+    for (int i = i0; i < i1; ++i) {
+        const int r = r0 + i;
+        const int rl = plan_role(ph, pairs, i, C);
         if (rl == -2) continue;
         if (rl >= 0) {
             const int slot = hb * max_pairs + rl;
-            items[item++] = WorkItem{r, slot * Nb, slot * Nb + ulen[slot], -2 - (i_row + 1)};
+            items[item++] = WorkItem{r, slot * Nb, slot * Nb + ph.ulen[rl], -2 - (i + 1)};
             continue;
         }
-        const int b0 = row_ptr[r], cnt = row_ptr[r + 1] - b0;
+        const int b0 = ph.rp[i], cnt = ph.rp[i + 1] - b0;
         const int n = chunks_of(cnt, C);
         if (n == 1) {
             items[item++] = WorkItem{r, b0, b0 + cnt, -1};
         } else {
             splits[spl++] = SplitRow{r, part, n, 0};
             for (int q = 0; q < n; ++q) {
-                const int s = b0 + (int)((int64_t)cnt * q / n);
+                const int sb = b0 + (int)((int64_t)cnt * q / n);
                 const int e = b0 + (int)((int64_t)cnt * (q + 1) / n);
-                items[item++] = WorkItem{r, s, e, part++};
+                items[item++] = WorkItem{r, sb, e, part++};
             }
         }
     }
-    if (tid == 0) {
-        hdr->info.n_items = n_items;
+    if (hb == 0 && tid == 0) {
+        hdr->info.n_items = n4[0];
         hdr->info.chunk_blocks = C;
-        hdr->info.n_split_rows = n_splits;
-        hdr->info.n_partials = n_parts;
+        hdr->info.n_split_rows = n4[2];
+        hdr->info.n_partials = n4[1];
         hdr->info.total_blocks = total;
         hdr->info.num_ctas = num_ctas;
-        hdr->info.n_row_pairs = n_pairs;
+        hdr->info.n_row_pairs = n4[3];
         hdr->info.kept_pairs = 0;
         hdr->info.predicted_imbalance = 0.f;
         hdr->info.reserved = 0;
@@ -1538,11 +1567,14 @@ size_t packed_kv_bytes(const Geo &g) {
 
 hipError_t launch_plan(const Geo &g, const int32_t *row_ptr, int chunk_mode, int num_ctas, int cap_items,
                        int cap_parts, const RowPairs &rp, PlanHeader *hdr, WorkItem *items, SplitRow *splits,
-                       hipStream_t s) {
+                       int32_t *head_counts, hipStream_t s) {
     const bool pairs = rp.max_pairs > 0;
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, g.BH * g.Nb, g.Nb, row_ptr, chunk_mode, num_ctas,
-                       cap_items, cap_parts, pairs ? rp.role : nullptr, pairs ? rp.ulen : nullptr, rp.max_pairs, hdr,
-                       items, splits);
+    if (g.Nb > kPlanMaxRows || rp.max_pairs > kPlanMaxPairs || g.BH <= 0) return hipErrorInvalidValue;
+    const int32_t *role = pairs ? rp.role : nullptr, *ulen = pairs ? rp.ulen : nullptr;
+    hipLaunchKernelGGL(plan_count_kernel, dim3(g.BH), dim3(kPlanThreads), 0, s, g.BH, g.Nb, row_ptr, chunk_mode,
+                       num_ctas, role, ulen, rp.max_pairs, head_counts);
+    hipLaunchKernelGGL(plan_emit_kernel, dim3(g.BH), dim3(kPlanThreads), 0, s, g.BH, g.Nb, row_ptr, chunk_mode,
+                       num_ctas, cap_items, cap_parts, role, ulen, rp.max_pairs, head_counts, hdr, items, splits);
     return hipGetLastError();
 }
 

@@ -118,7 +118,7 @@ hipError_t launch_row_pairs(const Geo &g, const int32_t *bsize, const int32_t *r
                            const RowPairs &rp, hipStream_t s);
 hipError_t launch_plan(const Geo &g, const int32_t *row_ptr, int chunk_mode, int num_ctas,
                        int cap_items, int cap_parts, const RowPairs &rp, PlanHeader *hdr, WorkItem *items,
-                       SplitRow *splits, hipStream_t s);
+                       SplitRow *splits, int32_t *head_counts, hipStream_t s);
 hipError_t launch_plan_stats(const Geo &g, const int32_t *row_ptr, const int32_t *col_idx, const int32_t *bsize,
                              int num_ctas, const WorkItem *items, PlanHeader *hdr, hipStream_t s);
 hipError_t launch_attention(const Geo &g, const void *q, const void *k, const void *v, void *o,
