@@ -546,13 +546,19 @@ __global__ __launch_bounds__(64 * kRowsPerGroup) __attribute__((amdgpu_waves_per
     // A lane whose E entries all lie in the row writes them as 16-byte
     // stores when row * Nk is a multiple of 4 (the row's masses and order
     // then start 16-byte aligned; the same for the whole wave).
-    if (E >= 4 && e0 + E <= Nk && ((row * Nk) & 3) == 0) {
+    bool stored = false;
+    if constexpr (E >= 4) {
+        if (e0 + E <= Nk && ((row * Nk) & 3) == 0) {
 #pragma unroll
-        for (int r = 0; r < E; r += 2) *reinterpret_cast<double2 *>(srow + e0 + r) = make_double2(v[r], v[r + 1]);
+            for (int r = 0; r < E; r += 2)
+                *reinterpret_cast<double2 *>(srow + e0 + r) = make_double2(v[r], v[r + 1]);
 #pragma unroll
-        for (int r = 0; r < E; r += 4)
-            *reinterpret_cast<int4 *>(orow + e0 + r) = make_int4(id[r], id[r + 1], id[r + 2], id[r + 3]);
-    } else {
+            for (int r = 0; r < E; r += 4)
+                *reinterpret_cast<int4 *>(orow + e0 + r) = make_int4(id[r], id[r + 1], id[r + 2], id[r + 3]);
+            stored = true;
+        }
+    }
+    if (!stored) {
 #pragma unroll
         for (int r = 0; r < E; ++r) {
             if (e0 + r < Nk) {
