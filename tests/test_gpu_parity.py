@@ -243,6 +243,79 @@ def test_equal_load_plan_balances_exactly(dev):
     assert imb <= 1.10
 
 
+def _host_plan_counts(rp, ci, Nb, BH, C, sizes, pairs_on):
+    """The balancer's counts recomputed on the host from the lists, by the rule
+    the plan states: a row of more than C kept blocks becomes ceil(cnt / C)
+    work items, each with a partial slot; with row pairs, neighbouring query
+    blocks of at most 64 tokens are paired two by two from the start of each
+    run of such blocks, and a pair is one item when its union list holds at
+    most C blocks.  Returns (items, partial slots, split rows, pairs)."""
+    firsts = []
+    if pairs_on:
+        i = 0
+        while i < Nb - 1:
+            if sizes[i] <= 64 and sizes[i + 1] <= 64:
+                firsts.append(i)
+                i += 2
+            else:
+                i += 1
+    items = parts = splits = npairs = 0
+    for bh in range(BH):
+        paired = set()
+        for i in firsts:
+            r = bh * Nb + i
+            union = set(ci[rp[r]:rp[r + 1]].tolist()) | set(ci[rp[r + 1]:rp[r + 2]].tolist())
+            if len(union) <= C:
+                paired.update((i, i + 1))
+                npairs += 1
+                items += 1
+        for i in range(Nb):
+            if i in paired:
+                continue
+            r = bh * Nb + i
+            cnt = int(rp[r + 1] - rp[r])
+            n = -(-cnt // C) if cnt > C else 1
+            items += n
+            if n > 1:
+                splits += 1
+                parts += n
+    return items, parts, splits, npairs
+
+
+@pytest.mark.parametrize("cid", [2, 4])
+def test_plan_counts_match_host(dev, cid):
+    """The plan's work-item, split-row, partial-slot and pair counts, its chunk
+    size and its total equal the balancer rule applied on the host to the
+    GPU's own lists: every chunk mode (automatic, unsplit, fixed 1, 3 and 7
+    blocks) with row pairs on and off on the mid size, and the automatic mode
+    on the 5-head 720p shard, whose long rows are split."""
+    w = WORKLOADS[cid]
+    q, k, v, _ = make_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    lay = BlockLayout(w.grid, w.tile)
+    sizes = [len(m) for m in lay.members]
+    lists = fva.route(qd, kd, w.p, w.kmin, w.budget, grid=w.grid, tile=w.tile)
+    g = gpu_lists_to_host(lists)
+    rp, ci = g["row_ptr"], g["col_idx"]
+    BH = w.B * w.H
+    modes = [(0, True), (0, False), (-1, True), (-1, False), (1, False), (3, False), (7, False)] if cid == 2 \
+        else [(0, True)]
+    for chunk, pairs in modes:
+        st = torch.zeros(fva.stats_bytes(qd, w.grid, w.tile, chunk_blocks=chunk), dtype=torch.uint8, device=dev)
+        fva.sparse_attn(qd, kd, vd, lists, stats=st, chunk_blocks=chunk, row_pairs=pairs)
+        torch.cuda.synchronize()
+        info, _ = fva.parse_stats(st)
+        total = int(rp[-1])
+        C = {0: max(16, -(-total // (8 * info.num_ctas))), -1: 2 ** 31 - 1}.get(chunk, chunk)
+        items, parts, splits, npairs = _host_plan_counts(rp, ci, lay.Nb, BH, C, sizes, pairs and chunk <= 0)
+        got = (info.n_items, info.n_partials, info.n_split_rows, info.n_row_pairs, info.chunk_blocks,
+               info.total_blocks)
+        print(f"\n[plan] config {cid} chunk {chunk} pairs {pairs}: {got}", flush=True)
+        assert got == (items, parts, splits, npairs, C, total), (chunk, pairs, got)
+        if cid == 4:
+            assert splits > 0
+
+
 def _small_case(grid, tile, H, d, dtype, seed, scale=1.0, B=1):
     N = grid[0] * grid[1] * grid[2]
     q = tiny_random((B, H, N, d), seed, dtype, scale)
